@@ -1,0 +1,194 @@
+"""Python binding of libcle.so, the cross-layer MoE expert step for MI355X.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels (or, for ``schedule_step``, its host C++).  Tensors are torch tensors
+on the GPU; PyTorch provides device memory and streams.  If ``libcle.so`` is
+missing or fails to load, importing this package raises -- there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcle.so")
+
+OK, EINVAL, EHIP, EWORKSPACE, EUNSUPPORTED = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+POLICY_B0_ALONE, POLICY_B1_LOCKSTEP, POLICY_CUMUTIL, POLICY_MAXUTIL, POLICY_DIFFPEAK = range(5)
+POLICIES = {"b0": 0, "b1": 1, "cumutil": 2, "maxutil": 3, "diffpeak": 4}
+OP_DISPATCH, OP_FFN = 1, 2
+MAX_E, MAX_MICROBATCHES, MAX_MAXUTIL_POOL, MAX_DESC = 1024, 64, 20, 64
+
+
+class CleError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def _load():
+    # torch ships a HIP runtime with the same soname as ROCm's; loading torch
+    # first makes libcle bind to that one runtime, so torch's streams and
+    # device pointers are valid in the library.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m cross_layer_expert_amd.build` (hipcc, gfx950)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+_lib = _load()
+
+_i32, _i64, _u64, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class FfnDesc(ctypes.Structure):
+    """Mirror of ``cle_ffn_desc``."""
+    _fields_ = [("layer", _i32), ("rows", _i32), ("offsets", _vp), ("xp", _vp), ("act", _vp),
+                ("yp", _vp), ("shared_rows", _i32), ("x_shared", _vp), ("act_shared", _vp),
+                ("y_shared", _vp)]
+
+
+_sig = {
+    "cle_route": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "cle_dispatch": (_i32, [_vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                            _vp, _sz, _vp]),
+    "cle_grouped_expert_ffn": (_i32, [ctypes.POINTER(FfnDesc), _i32, _vp, _vp, _vp, _vp, _i32,
+                                      _i32, _i32, _i32, _i32, _i32, _vp, _sz,
+                                      ctypes.POINTER(_vp), _vp]),
+    "cle_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp]),
+    "cle_workload_stats": (_i32, [_vp, _i32, _i32, _i32, _u64, _vp, _vp, _vp]),
+    "cle_schedule_step": (_i32, [ctypes.POINTER(_i32), _i32, _i32, _u64, _i32, _i32,
+                                 ctypes.POINTER(_u64)]),
+    "cle_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "cle_status_string": (ctypes.c_char_p, [_i32]),
+    "cle_version": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def status_string(s: int) -> str:
+    return _lib.cle_status_string(int(s)).decode()
+
+
+def version() -> str:
+    return _lib.cle_version().decode()
+
+
+def _check(fn, st):
+    if st != OK:
+        raise CleError(fn, st)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or None."""
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def workspace_bytes(op, T=0, E=1, k=1, n_shared=0, n_desc=1) -> int:
+    return int(_lib.cle_workspace_bytes(op, T, E, k, n_shared, n_desc))
+
+
+# ---------------------------------------------------------------- entry points
+def route(logits, k, topk_idx, topk_gate, stream=None):
+    T, E = logits.shape
+    _check("cle_route", _lib.cle_route(_ptr(logits), T, E, k, _ptr(topk_idx), _ptr(topk_gate),
+                                       _stream(stream)))
+
+
+def dispatch(topk_idx, E, x, counts, offsets, dest, src, xp, ws, stream=None):
+    T, k = topk_idx.shape
+    H = x.shape[1]
+    _check("cle_dispatch", _lib.cle_dispatch(
+        _ptr(topk_idx), T, k, E, _ptr(x), H, _dt(x), _ptr(counts), _ptr(offsets), _ptr(dest),
+        _ptr(src), _ptr(xp), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def make_desc(layer, rows, offsets, xp, act, yp, shared_rows=0, x_shared=None, act_shared=None,
+              y_shared=None) -> FfnDesc:
+    return FfnDesc(layer, rows, _ptr(offsets), _ptr(xp), _ptr(act), _ptr(yp), shared_rows,
+                   _ptr(x_shared), _ptr(act_shared), _ptr(y_shared))
+
+
+def grouped_expert_ffn(descs, w13, w2, ws, w13_shared=None, w2_shared=None, events=None,
+                       stream=None):
+    """descs: list of FfnDesc.  w13 [L, E, 2I, H], w2 [L, E, H, I].
+    events: None or 3 raw hipEvent_t handles (ints)."""
+    L, E, I2, H = w13.shape
+    ns = 0 if w13_shared is None else w13_shared.shape[1]
+    arr = (FfnDesc * len(descs))(*descs)
+    ev = None
+    if events is not None:
+        ev = (_vp * 3)(*events)
+    _check("cle_grouped_expert_ffn", _lib.cle_grouped_expert_ffn(
+        arr, len(descs), _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared), L, E, ns, H,
+        I2 // 2, _dt(w13), _ptr(ws), ws.numel() * ws.element_size(), ev, _stream(stream)))
+
+
+def combine(yp, dest, topk_gate, y, y_shared=None, residual=None, stream=None):
+    T, k = topk_gate.shape
+    H = y.shape[-1]
+    ns = 0 if y_shared is None else y_shared.shape[0]
+    _check("cle_combine", _lib.cle_combine(
+        _ptr(yp), _ptr(dest), _ptr(topk_gate), T, k, H, _ptr(y_shared), ns, _ptr(residual),
+        _ptr(y), _dt(y), _stream(stream)))
+
+
+def workload_stats(counts, D, runset_mask, w, acc=None, stream=None):
+    n, E = counts.shape
+    _check("cle_workload_stats", _lib.cle_workload_stats(
+        _ptr(counts), n, E, D, int(runset_mask), _ptr(w), _ptr(acc), _stream(stream)))
+
+
+def schedule_step(w, ready_mask, m, policy) -> int:
+    """w: host int32 array [n, D].  Returns the RunSet bitmask."""
+    w = np.ascontiguousarray(w, dtype=np.int32)
+    n, D = w.shape
+    out = _u64(0)
+    _check("cle_schedule_step", _lib.cle_schedule_step(
+        w.ctypes.data_as(ctypes.POINTER(_i32)), n, D, int(ready_mask), m, int(policy),
+        ctypes.byref(out)))
+    return int(out.value)
+
+
+def schedule_step_raw(w_ptr, n, D, ready_mask, m, policy) -> int:
+    """Same as schedule_step with w given as a host address (pinned buffer)."""
+    out = _u64(0)
+    _check("cle_schedule_step", _lib.cle_schedule_step(
+        ctypes.cast(w_ptr, ctypes.POINTER(_i32)), n, D, int(ready_mask), m, int(policy),
+        ctypes.byref(out)))
+    return int(out.value)
+
+
+def mask_of(ids) -> int:
+    m = 0
+    for j in ids:
+        m |= 1 << int(j)
+    return m
+
+
+def ids_of(mask: int) -> list:
+    return [j for j in range(64) if mask >> j & 1]

@@ -1,0 +1,61 @@
+// Internal helpers shared by the libcle translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cle.h"
+
+namespace cle {
+
+constexpr int kWave = 64;
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Launch-status helper: any error left by the launches maps to CLE_EHIP.
+inline cle_status launch_status() {
+  return hipGetLastError() == hipSuccess ? CLE_OK : CLE_EHIP;
+}
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- bf16
+// IEEE bfloat16 held as its 16-bit pattern.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------- workspace layout
+// Dispatch workspace: per-chunk per-expert counts, then bases.
+constexpr int kDispatchChunk = 1024;  // assignments per histogram block
+
+inline int64_t dispatch_chunks(int64_t A) { return (A + kDispatchChunk - 1) / kDispatchChunk; }
+
+// FFN workspace: segment table + totals.
+struct Seg {
+  const uint16_t* a;    // phase-1 A rows (bf16 or f32 storage; byte pointer semantics by dtype)
+  void* act;            // phase-1 output / phase-2 A rows
+  void* y;              // phase-2 output rows
+  const void* w13;      // [2I, H]
+  const void* w2;       // [H, I]
+  int32_t rows;
+  int32_t t1;           // first phase-1 tile of this segment
+  int32_t t2;           // first phase-2 tile of this segment
+  int32_t pad_;
+};
+static_assert(sizeof(Seg) == 56, "Seg layout");
+
+constexpr size_t kFfnHeader = 256;  // totals live in the first 256 bytes
+
+}  // namespace cle

@@ -1,0 +1,123 @@
+// Gate-weighted combine of each token's expert outputs, plus shared experts
+// and the residual.  "EasyBalance: Cross-Layer Load Balancing in Distributed
+// MoE Inference", Eq. (1): MLP(h'_l) = sum_{i in I_l} W_{l,i} expert_i(h'_l),
+// and §2.1: h_{l+1} = h'_l + MLP(h'_l).
+//
+// One wavefront per token; each lane owns 16-byte column groups.  The sum is
+// taken in float32 in a fixed order (slots, shared experts, residual) and
+// rounded once, so it is deterministic and a gather, never a scatter-add.
+#include "cle_internal.h"
+
+namespace cle {
+namespace {
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t* p, float* f) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(uint16_t* p, const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(f[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(f[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* f) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    f[0] = v.x;
+    f[1] = v.y;
+    f[2] = v.z;
+    f[3] = v.w;
+  }
+  __device__ static void store(float* p, const float* f) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp,
+                                                      const int* __restrict__ dest,
+                                                      const float* __restrict__ gate, int T_,
+                                                      int k, int H, const T* __restrict__ y_shared,
+                                                      int n_shared, const T* residual, T* y) {
+  constexpr int N = Vec<T>::N;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T_) return;
+  const int* drow = dest + static_cast<int64_t>(t) * k;
+  const float* grow = gate + static_cast<int64_t>(t) * k;
+  for (int c = lane * N; c < H; c += kWave * N) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+    for (int s = 0; s < k; ++s) {
+      const int d = drow[s];
+      if (d < 0) continue;
+      const float g = grow[s];
+      float v[N];
+      Vec<T>::load(yp + static_cast<int64_t>(d) * H + c, v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    for (int q = 0; q < n_shared; ++q) {
+      float v[N];
+      Vec<T>::load(y_shared + (static_cast<int64_t>(q) * T_ + t) * H + c, v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+    if (residual) {
+      float v[N];
+      Vec<T>::load(residual + static_cast<int64_t>(t) * H + c, v);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] += v[i];
+    }
+    Vec<T>::store(y + static_cast<int64_t>(t) * H + c, acc);
+  }
+}
+
+}  // namespace
+}  // namespace cle
+
+extern "C" cle_status cle_combine(const void* yp, const int32_t* dest, const float* topk_gate,
+                                  int32_t T, int32_t k, int32_t H, const void* y_shared,
+                                  int32_t n_shared, const void* residual, void* y, cle_dtype dt,
+                                  void* stream) {
+  using namespace cle;
+  if (T < 0 || k < 1 || H < 8 || H % 8 || n_shared < 0) return CLE_EINVAL;
+  if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
+  if (T == 0) return CLE_OK;
+  if (!yp || !dest || !topk_gate || !y) return CLE_EINVAL;
+  if (n_shared > 0 && !y_shared) return CLE_EINVAL;
+  if (!aligned(yp, 16) || !aligned(y, 16) || (y_shared && !aligned(y_shared, 16)) ||
+      (residual && !aligned(residual, 16)))
+    return CLE_EINVAL;
+  const dim3 grid((T + 3) / 4), block(256);
+  hipStream_t s = as_stream(stream);
+  if (dt == CLE_BF16)
+    combine_kernel<uint16_t><<<grid, block, 0, s>>>(
+        static_cast<const uint16_t*>(yp), dest, topk_gate, T, k, H,
+        static_cast<const uint16_t*>(y_shared), n_shared, static_cast<const uint16_t*>(residual),
+        static_cast<uint16_t*>(y));
+  else
+    combine_kernel<float><<<grid, block, 0, s>>>(
+        static_cast<const float*>(yp), dest, topk_gate, T, k, H,
+        static_cast<const float*>(y_shared), n_shared, static_cast<const float*>(residual),
+        static_cast<float*>(y));
+  return launch_status();
+}

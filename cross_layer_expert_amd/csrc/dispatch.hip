@@ -1,0 +1,214 @@
+// Dispatch: per-expert histogram, exclusive scan, stable permutation and row
+// gather -- the single-GPU form of the expert-parallel all-to-all dispatch
+// ("EasyBalance: Cross-Layer Load Balancing in Distributed MoE Inference",
+// §2.2; per-expert token counts T_e as in section 1 of the EP load-balancing
+// atlas page "系统侧负载均衡：EPLB、LPLB、UltraEP 与 MoonEP").
+//
+// Assignment a = t*k + s goes to row dest[a] = offsets[e] + (number of
+// earlier assignments to the same expert): a stable counting sort.
+//
+//   1. count   one block per 1024-assignment chunk: LDS histogram
+//   2. scan    one block: per-expert prefix over chunks, prefix over experts
+//   3. scatter one block per chunk: in-order ranks from wavefront ballots
+//              (lanes that share an expert id find each other with one ballot
+//              per id bit; rank = popcount of the lower lanes in the group)
+//   4. gather  one wavefront per destination row: xp[p] = x[src[p] / k]
+// Integer only; every output is exact and deterministic.
+#include "cle_internal.h"
+
+namespace cle {
+namespace {
+
+constexpr int kChunkWaves = 4;
+constexpr int kPerWave = kDispatchChunk / kChunkWaves;  // 256 assignments per wave
+
+__global__ __launch_bounds__(256) void dispatch_count(const int* __restrict__ idx, int64_t A,
+                                                      int E, int* __restrict__ chunk_hist) {
+  __shared__ int hist[CLE_MAX_E];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
+  for (int i = threadIdx.x; i < kDispatchChunk; i += blockDim.x) {
+    const int64_t a = base + i;
+    if (a < A) {
+      const int e = idx[a];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  int* out = chunk_hist + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = hist[e];
+}
+
+// Turns chunk counts into absolute chunk bases in place and writes counts
+// and offsets.
+__global__ __launch_bounds__(1024) void dispatch_scan(int* __restrict__ chunk_hist, int64_t chunks,
+                                                      int E, int* __restrict__ counts,
+                                                      int* __restrict__ offsets) {
+  __shared__ int tot[CLE_MAX_E];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int64_t c = 0; c < chunks; ++c) {
+      int* p = chunk_hist + c * E + e;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan of tot[0..E) with one value per thread (E <= 1024)
+  const int v = tid < E ? tot[tid] : 0;
+  part[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  const int excl = part[tid] - v;
+  if (tid < E) {
+    counts[tid] = v;
+    offsets[tid] = excl;
+  }
+  if (tid == E - 1) offsets[E] = part[tid];
+  __syncthreads();
+  if (tid < E) tot[tid] = excl;
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x)
+    for (int64_t c = 0; c < chunks; ++c) chunk_hist[c * E + e] += tot[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter(const int* __restrict__ idx, int64_t A,
+                                                        int E, int id_bits,
+                                                        const int* __restrict__ chunk_base,
+                                                        int* __restrict__ dest,
+                                                        int* __restrict__ src) {
+  __shared__ int wcount[kChunkWaves][CLE_MAX_E];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  for (int i = threadIdx.x; i < kChunkWaves * E; i += blockDim.x) wcount[i / E][i % E] = 0;
+  __syncthreads();
+  const int64_t wbase = static_cast<int64_t>(blockIdx.x) * kDispatchChunk +
+                        static_cast<int64_t>(wave) * kPerWave;
+  // pass 1: per-wave counts
+  for (int it = 0; it < kPerWave / kWave; ++it) {
+    const int64_t a = wbase + it * kWave + lane;
+    if (a < A) {
+      const int e = idx[a];
+      if (e >= 0 && e < E) atomicAdd(&wcount[wave][e], 1);
+    }
+  }
+  __syncthreads();
+  // per expert: absolute base of each wave's sub-range
+  const int* cb = chunk_base + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = cb[e];
+    for (int w = 0; w < kChunkWaves; ++w) {
+      const int v = wcount[w][e];
+      wcount[w][e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  // pass 2: ranks in assignment order
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int it = 0; it < kPerWave / kWave; ++it) {
+    const int64_t a = wbase + it * kWave + lane;
+    const bool in = a < A;
+    const int e = in ? idx[a] : -1;
+    const bool valid = in && e >= 0 && e < E;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      match &= bit ? bb : ~bb;
+    }
+    int d = -1;
+    if (valid) {
+      const int rank = __popcll(match & lt_mask);
+      d = wcount[wave][e] + rank;
+    }
+    // all lanes have read their base before the group leaders advance it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (valid) {
+      const bool leader = (match >> lane) == 1ull;  // highest lane of its group
+      if (leader) wcount[wave][e] += __popcll(match);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (in) {
+      dest[a] = d;
+      if (valid) src[d] = static_cast<int>(a);
+    }
+  }
+}
+
+// One wavefront per destination row; VEC elements of T per 16-byte access.
+template <typename T>
+__global__ __launch_bounds__(256) void dispatch_gather(const T* __restrict__ x, int64_t A, int k,
+                                                       int H, const int* __restrict__ offsets,
+                                                       int E, int* __restrict__ src,
+                                                       T* __restrict__ xp) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t p = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (p >= A) return;
+  const int64_t valid_rows = offsets[E];
+  uint4* out = reinterpret_cast<uint4*>(xp + p * H);
+  const int nvec = H / VEC;
+  if (p < valid_rows) {
+    const int64_t t = src[p] / k;
+    const uint4* in = reinterpret_cast<const uint4*>(x + t * H);
+    for (int c = lane; c < nvec; c += kWave) out[c] = in[c];
+  } else {
+    if (lane == 0) src[p] = -1;
+    for (int c = lane; c < nvec; c += kWave) out[c] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+}  // namespace
+}  // namespace cle
+
+extern "C" cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                   const void* x, int32_t H, cle_dtype dt, int32_t* counts,
+                                   int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  using namespace cle;
+  if (T < 0 || k < 1 || E < 1 || E > CLE_MAX_E || H < 8 || H % 8) return CLE_EINVAL;
+  if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
+  if (!counts || !offsets) return CLE_EINVAL;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (A > INT32_MAX) return CLE_EUNSUPPORTED;
+  if (A > 0 && (!topk_idx || !x || !dest || !src || !xp)) return CLE_EINVAL;
+  if (!aligned(x, 16) || !aligned(xp, 16)) return CLE_EINVAL;
+  const size_t need = cle_workspace_bytes(CLE_OP_DISPATCH, T, E, k, 0, 1);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return CLE_EWORKSPACE;
+  hipStream_t s = as_stream(stream);
+  int64_t chunks = dispatch_chunks(A);
+  int* hist = static_cast<int*>(ws);
+  if (chunks > 0) {
+    dispatch_count<<<dim3(static_cast<unsigned>(chunks)), dim3(256), 0, s>>>(topk_idx, A, E, hist);
+  }
+  dispatch_scan<<<dim3(1), dim3(1024), 0, s>>>(hist, chunks, E, counts, offsets);
+  if (A == 0) return launch_status();
+  int id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  dispatch_scatter<<<dim3(static_cast<unsigned>(chunks)), dim3(256), 0, s>>>(
+      topk_idx, A, E, id_bits, hist, dest, src);
+  const dim3 ggrid(static_cast<unsigned>((A + 3) / 4));
+  if (dt == CLE_BF16)
+    dispatch_gather<uint16_t><<<ggrid, dim3(256), 0, s>>>(
+        static_cast<const uint16_t*>(x), A, k, H, offsets, E, src, static_cast<uint16_t*>(xp));
+  else
+    dispatch_gather<float><<<ggrid, dim3(256), 0, s>>>(static_cast<const float*>(x), A, k, H,
+                                                       offsets, E, src, static_cast<float*>(xp));
+  return launch_status();
+}

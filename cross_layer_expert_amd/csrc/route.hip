@@ -1,0 +1,113 @@
+// Router top-k with renormalised softmax gates.
+// "EasyBalance: Cross-Layer Load Balancing in Distributed MoE Inference",
+// §2.1: W_l, I_l = topk(G(h'_l)); here the router scores are given.
+//
+// One wavefront per token.  Each lane holds up to VPL logits as 64-bit keys
+//   key = (order-preserving bits of the logit) << 32 | (0xffffffff - expert)
+// so that an unsigned max picks the largest logit and, among equal logits,
+// the smallest expert id.  Each of the k rounds is one wave-wide max; the
+// winner's key is cleared.  Key 0 never belongs to a finite logit.
+#include "cle_internal.h"
+
+namespace cle {
+namespace {
+
+constexpr int kRouteWaves = 4;  // tokens per 256-thread block
+
+__device__ __forceinline__ uint32_t ord_bits(float z) {
+  if (z == 0.0f) z = 0.0f;  // -0.0 and +0.0 are the same logit
+  uint32_t b = __float_as_uint(z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ord_bits(uint32_t o) {
+  uint32_t b = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(b);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
+                                                    int E, int k, int* __restrict__ idx,
+                                                    float* __restrict__ gate) {
+  __shared__ float zsel[kRouteWaves][CLE_MAX_E];
+  __shared__ int esel[kRouteWaves][CLE_MAX_E];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * kRouteWaves + wave;
+  if (t >= T) return;  // whole wavefront leaves; no block barrier follows
+
+  const float* row = logits + static_cast<int64_t>(t) * E;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane * VPL + v;
+    key[v] = 0;
+    if (e < E)
+      key[v] = (static_cast<uint64_t>(ord_bits(row[e])) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
+  }
+
+  double z0 = 0.0, total = 0.0;
+  for (int s = 0; s < k; ++s) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
+    best = wave_max_u64(best);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (key[v] == best) key[v] = 0;
+    const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+    const float z = from_ord_bits(static_cast<uint32_t>(best >> 32));
+    // every lane holds the same (z, e); all lanes store the same value
+    zsel[wave][s] = z;
+    esel[wave][s] = e;
+    if (s == 0) z0 = static_cast<double>(z);
+    total += exp(static_cast<double>(z) - z0);  // slot order
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  int* irow = idx + static_cast<int64_t>(t) * k;
+  float* grow = gate + static_cast<int64_t>(t) * k;
+  for (int s = lane; s < k; s += kWave) {
+    const double ex = exp(static_cast<double>(zsel[wave][s]) - z0);
+    grow[s] = static_cast<float>(ex / total);
+    irow[s] = esel[wave][s];
+  }
+}
+
+}  // namespace
+}  // namespace cle
+
+extern "C" cle_status cle_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                                int32_t* topk_idx, float* topk_gate, void* stream) {
+  using namespace cle;
+  if (T < 0 || E < 1 || E > CLE_MAX_E || k < 1 || k > E) return CLE_EINVAL;
+  if (T == 0) return CLE_OK;
+  if (!logits || !topk_idx || !topk_gate) return CLE_EINVAL;
+  const dim3 grid((T + kRouteWaves - 1) / kRouteWaves), block(256);
+  hipStream_t s = as_stream(stream);
+  const int vpl = (E + kWave - 1) / kWave;
+  if (vpl <= 1)
+    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+  else if (vpl <= 2)
+    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+  else if (vpl <= 4)
+    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+  else if (vpl <= 8)
+    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+  else
+    route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+  return launch_status();
+}

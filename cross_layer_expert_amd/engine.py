@@ -1,0 +1,157 @@
+"""Algorithm 1 of EasyBalance driven through libcle.
+
+"EasyBalance: Cross-Layer Load Balancing in Distributed MoE Inference",
+Algorithm 1 (§4.2): every micro-batch T_j keeps its current layer l_j; each
+step routes and dispatches the micro-batches run in the previous step
+(AttnRouteDispatch), picks RunSet_i from the pool (Schedule(S, m)), runs the
+experts of every RunSet member -- each at its own layer -- in one grouped
+launch and combines them (MoECompute_Combine), then advances l_j of the
+members and drops finished micro-batches.
+
+Attention is outside the MoE step and taken as the identity, so a layer is
+h <- h + MoE_l(h).  Router logits are inputs (one [T, E] block per
+(micro-batch, layer)).  All per-micro-batch state lives in HBM; the only
+device-to-host traffic per step is the n x D workload matrix the host
+scheduler reads (n*D int32).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (BF16, OP_DISPATCH, OP_FFN, combine, dispatch, grouped_expert_ffn, ids_of,
+               make_desc, mask_of, route, schedule_step_raw, workload_stats, workspace_bytes)
+
+
+class Engine:
+    """Device-resident state of n micro-batches moving through an L-layer MoE stack.
+
+    weights: (w13 [L,E,2I,H], w2 [L,E,H,I], w13_shared | None, w2_shared | None),
+    logits: tensor [n, L, T, E] float32 on the device, h0: tensor [n, T, H].
+    """
+
+    def __init__(self, weights, logits, h0, D, k, policy, m, start_layers=None, stream=None):
+        self.w13, self.w2, self.w13s, self.w2s = weights
+        self.L, self.E, I2, self.H = self.w13.shape
+        self.I = I2 // 2
+        self.ns = 0 if self.w13s is None else self.w13s.shape[1]
+        self.logits = logits
+        self.n, self.T = h0.shape[0], h0.shape[1]
+        self.k, self.D, self.policy, self.m = k, D, int(policy), m
+        self.start = list(start_layers) if start_layers else [0] * self.n
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        dev, dt = h0.device, h0.dtype
+        n, T, H, I, E, A = self.n, self.T, self.H, self.I, self.E, self.T * k
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.h0 = h0
+        self.h = h0.clone()
+        self.idx = torch.empty((n, T, k), **i32)
+        self.gates = torch.empty((n, T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.zeros((n, E), **i32)
+        self.offsets = torch.zeros((n, E + 1), **i32)
+        self.dest = torch.empty((n, A), **i32)
+        self.src = torch.empty((n, A), **i32)
+        self.xp = torch.empty((n, A, H), dtype=dt, device=dev)
+        self.act = torch.empty((n, A, I), dtype=dt, device=dev)
+        self.yp = torch.empty((n, A, H), dtype=dt, device=dev)
+        if self.ns:
+            self.act_sh = torch.empty((n, self.ns, T, I), dtype=dt, device=dev)
+            self.y_sh = torch.empty((n, self.ns, T, H), dtype=dt, device=dev)
+        else:
+            self.act_sh = self.y_sh = None
+        self.w_dev = torch.zeros((n, D), **i32)
+        self.acc = torch.zeros(4, dtype=torch.int64, device=dev)
+        self.w_host = torch.zeros((n, D), dtype=torch.int32).pin_memory()
+        self.ws_dispatch = torch.empty(
+            max(256, workspace_bytes(OP_DISPATCH, T, E, k)) // 4, dtype=torch.int32, device=dev)
+        self.ws_ffn = torch.empty(
+            max(256, workspace_bytes(OP_FFN, 0, E, 1, self.ns, n)) // 4, dtype=torch.int32,
+            device=dev)
+        self.descs = [self._desc(j) for j in range(n)]
+        self.reset()
+
+    def _desc(self, j):
+        d = make_desc(0, self.T * self.k, self.offsets[j], self.xp[j], self.act[j], self.yp[j])
+        if self.ns:
+            d.shared_rows = self.T
+            d.x_shared = self.h[j].data_ptr()
+            d.act_shared = self.act_sh[j].data_ptr()
+            d.y_shared = self.y_sh[j].data_ptr()
+        return d
+
+    def reset(self, h0=None):
+        """Back to the start: every micro-batch at its first layer, stats cleared."""
+        self.h.copy_(self.h0 if h0 is None else h0)
+        self.acc.zero_()
+        self.l = list(self.start)
+        self.S = [j for j in range(self.n) if self.l[j] < self.L]
+        self.prev = list(self.S)
+        self.trace = []
+
+    @property
+    def done(self) -> bool:
+        return not self.S
+
+    # ------------------------------------------------------------ one step
+    def route_dispatch(self, j):
+        """AttnRouteDispatch for micro-batch j at its current layer."""
+        s = self.stream
+        route(self.logits[j, self.l[j]], self.k, self.idx[j], self.gates[j], stream=s)
+        dispatch(self.idx[j], self.E, self.h[j], self.counts[j], self.offsets[j], self.dest[j],
+                 self.src[j], self.xp[j], self.ws_dispatch, stream=s)
+
+    def schedule(self) -> list:
+        """Workloads to the host, then Schedule(S, m) in the host library."""
+        s = self.stream
+        workload_stats(self.counts, self.D, 0, self.w_dev, stream=s)
+        self.w_host.copy_(self.w_dev, non_blocking=True)
+        s.synchronize()
+        R = schedule_step_raw(self.w_host.data_ptr(), self.n, self.D, mask_of(self.S), self.m,
+                              self.policy)
+        return ids_of(R)
+
+    def moe_compute_combine(self, R, events=None):
+        """MoECompute_Combine: one grouped expert launch for every member of R
+        (each at its own layer), then the Eq. (1) combine + residual."""
+        s = self.stream
+        workload_stats(self.counts, self.D, mask_of(R), self.w_dev, self.acc, stream=s)
+        descs = []
+        for j in R:
+            d = self.descs[j]
+            d.layer = self.l[j]
+            descs.append(d)
+        grouped_expert_ffn(descs, self.w13, self.w2, self.ws_ffn, self.w13s, self.w2s,
+                           events=events, stream=s)
+        for j in R:
+            combine(self.yp[j], self.dest[j], self.gates[j], self.h[j],
+                    y_shared=None if self.y_sh is None else self.y_sh[j], residual=self.h[j],
+                    stream=s)
+
+    def step(self, events=None) -> list:
+        """One iteration of the Algorithm 1 loop; returns RunSet_i."""
+        for j in self.prev:
+            if self.l[j] < self.L:
+                self.route_dispatch(j)
+        R = self.schedule()
+        layers = [self.l[j] for j in R]
+        self.moe_compute_combine(R, events=events)
+        self.trace.append((tuple(R), tuple(layers)))
+        for j in R:
+            self.l[j] += 1
+        self.S = [j for j in self.S if self.l[j] < self.L]
+        self.prev = R
+        return R
+
+    def run(self):
+        while self.S:
+            self.step()
+        return self
+
+    def stats(self):
+        """(work, effective workload, sum of members' own peaks, steps) and u."""
+        a = [int(v) for v in self.acc.cpu()]
+        u = a[0] / (self.D * a[1]) if a[1] else 0.0
+        return a, u
+
+    def expert_tokens(self, R) -> int:
+        return len(R) * self.T * (self.k + self.ns)

@@ -1,0 +1,234 @@
+/*
+ * cle.h -- C ABI of libcle.so, the cross-layer MoE expert step for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The step is the hot path of EasyBalance ("EasyBalance: Cross-Layer Load
+ * Balancing in Distributed MoE Inference", arXiv 2608.07964v1): route the
+ * tokens of several micro-batches, dispatch them to expert-grouped buffers,
+ * measure the per-device-group workload, pick which micro-batches run now
+ * (Algorithm 1, Schedule(S, m)), run one grouped SwiGLU expert launch that
+ * covers micro-batches sitting at different layers, and combine the expert
+ * outputs with the routing weights (Eq. (1)).
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the caller allocates and frees every buffer.  The library
+ *    never allocates device memory; scratch comes from a caller workspace
+ *    sized by cle_workspace_bytes().
+ *  - Pointers are device pointers unless marked HOST.
+ *  - Tensors are dense row-major.  bf16 tensors hold IEEE bfloat16 bit
+ *    patterns; gates are float32; indices are int32.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every entry point
+ *    except cle_schedule_step, cle_workspace_bytes and cle_status_string only
+ *    enqueues work on that stream and returns without waiting.
+ *  - Errors: arguments are validated on the host before anything is
+ *    enqueued; on error nothing is written and a negative status returns.
+ *    Device-side contents (expert ids) cannot be validated on the host; the
+ *    kernels stay in bounds whatever they hold (see cle_dispatch).
+ *  - Determinism: every output is bitwise reproducible and independent of how
+ *    micro-batches are grouped into one cle_grouped_expert_ffn call.  No
+ *    floating-point atomics are used.
+ */
+#ifndef CLE_H
+#define CLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t cle_status;
+#define CLE_OK 0
+#define CLE_EINVAL (-1)        /* bad argument (shape, size, null pointer, enum) */
+#define CLE_EHIP (-2)          /* a HIP runtime call failed */
+#define CLE_EWORKSPACE (-3)    /* workspace missing or too small */
+#define CLE_EUNSUPPORTED (-4)  /* valid but beyond this build's limits */
+
+typedef enum { CLE_BF16 = 0, CLE_F32 = 1 } cle_dtype;
+
+/* RunSet policies.  B0 and B1 are baselines; the others are the three
+ * heuristics of the paper, §5.2. */
+typedef enum {
+  CLE_POLICY_B0_ALONE = 0,     /* one micro-batch per step: no cross-layer combination */
+  CLE_POLICY_B1_LOCKSTEP = 1,  /* every ready micro-batch */
+  CLE_POLICY_CUMUTIL = 2,
+  CLE_POLICY_MAXUTIL = 3,
+  CLE_POLICY_DIFFPEAK = 4
+} cle_policy;
+
+/* Workspace-owning operations, for cle_workspace_bytes(). */
+typedef enum { CLE_OP_DISPATCH = 1, CLE_OP_FFN = 2 } cle_op;
+
+/* Library limits. */
+#define CLE_MAX_E 1024            /* experts per layer */
+#define CLE_MAX_MICROBATCHES 64   /* n: bits of a RunSet mask */
+#define CLE_MAX_MAXUTIL_POOL 20   /* MaxUtil enumerates 2^|S| subsets */
+#define CLE_MAX_DESC 64           /* micro-batches in one grouped FFN call */
+
+/*
+ * cle_route -- router top-k with renormalised softmax gates.
+ * Paper §2.1: W_l, I_l = topk(G(h'_l)); the router scores (logits) are given.
+ *
+ *   logits    [T, E] float32, finite.
+ *   topk_idx  [T, k] int32 out: slot s holds the s-th expert in the order
+ *             (logit descending, expert id ascending); -0.0 equals +0.0.
+ *   topk_gate [T, k] float32 out: g_s = exp(z_s - z_0) / sum_r exp(z_r - z_0)
+ *             over the k selected logits, evaluated in float64 (sum in slot
+ *             order) and rounded once to float32.
+ * Requires 1 <= k <= E <= CLE_MAX_E, T >= 0 (T == 0 enqueues nothing).
+ */
+cle_status cle_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                     int32_t* topk_idx, float* topk_gate, void* stream);
+
+/*
+ * cle_dispatch -- per-expert histogram, exclusive scan, stable permutation
+ * and row gather: the local form of the expert-parallel all-to-all dispatch
+ * (paper §2.2; per-expert token counts T_e as in the EP load-balancing atlas
+ * page, section 1).
+ *
+ *   topk_idx [T, k] int32: expert of assignment a = t*k + s.
+ *   x        [T, H] (dt): token rows.
+ *   counts   [E] int32 out: assignments per expert.
+ *   offsets  [E+1] int32 out: exclusive prefix sum of counts.
+ *   dest     [T*k] int32 out: dest[a] = offsets[e] + #{a' < a : idx[a'] = e}.
+ *   src      [T*k] int32 out: inverse permutation, src[dest[a]] = a.
+ *   xp       [T*k, H] (dt) out: xp[p] = x[src[p] / k].
+ *   ws       workspace of at least cle_workspace_bytes(CLE_OP_DISPATCH, T, E, k, ...).
+ * An expert id outside [0, E) is dropped: it is counted nowhere, its dest is
+ * -1, and the trailing rows p >= offsets[E] get src = -1 and zero xp rows.
+ * Requires H % 8 == 0, 1 <= k, 1 <= E <= CLE_MAX_E.
+ */
+cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                        const void* x, int32_t H, cle_dtype dt,
+                        int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
+                        void* xp, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One micro-batch of a grouped expert launch.  `layer` selects that layer's
+ * expert weights, so micro-batches at different layers share one launch
+ * (paper §4.1: workloads of several layers executed in one step).
+ */
+typedef struct {
+  int32_t layer;            /* in [0, L) */
+  int32_t rows;             /* rows of xp / act / yp (= T*k of the micro-batch) */
+  const int32_t* offsets;   /* [E+1] from cle_dispatch */
+  const void* xp;           /* [rows, H] (dt) */
+  void* act;                /* [rows, I] (dt) out: silu(G) * U */
+  void* yp;                 /* [rows, H] (dt) out: expert outputs, one per assignment */
+  int32_t shared_rows;      /* rows of x_shared (0 when n_shared == 0) */
+  const void* x_shared;     /* [shared_rows, H] (dt), rows for the shared experts */
+  void* act_shared;         /* [n_shared, shared_rows, I] (dt) out */
+  void* y_shared;           /* [n_shared, shared_rows, H] (dt) out */
+} cle_ffn_desc;
+
+/*
+ * cle_grouped_expert_ffn -- SwiGLU experts for every (micro-batch, expert)
+ * segment of all descs, in one grouped launch per GEMM phase.
+ * The expert form is SwiGLU with intermediate I, no biases:
+ *   [G | U] = X_s W13[l,e]^T,  Act = silu(G) * U,  Y = Act W2[l,e]^T,
+ * silu(v) = v / (1 + exp(-v)); segment X_s = xp[offsets[e] : offsets[e+1]].
+ * Paper Eq. (1) leaves expert_i abstract; the SwiGLU form is the workload's.
+ *
+ *   d          HOST array of n_desc descriptors (1 <= n_desc <= CLE_MAX_DESC).
+ *   w13        [L, E, 2I, H] (dt): rows [0, I) gate, rows [I, 2I) up.
+ *   w2         [L, E, H, I] (dt).
+ *   w13_shared [L, n_shared, 2I, H], w2_shared [L, n_shared, H, I]: always-on
+ *              shared experts (gate weight 1), applied to every x_shared row;
+ *              NULL when n_shared == 0.
+ *   bf16: fp32 accumulation; Act and Y rounded to bf16 (nearest even).
+ *   f32 : fp32 throughout.
+ *   phase_events: NULL, or HOST array of 3 hipEvent_t recorded on `stream`
+ *              after the planning kernel, after the gate/up phase and after
+ *              the down phase (for measurement).
+ * Rows of each segment are computed with one fixed instruction sequence, so
+ * a row's result does not depend on the other segments in the launch.
+ * Requires I % 64 == 0, and H % 128 == 0 for bf16 or H % 64 == 0 for f32.
+ */
+cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_desc,
+                                  const void* w13, const void* w2,
+                                  const void* w13_shared, const void* w2_shared,
+                                  int32_t L, int32_t E, int32_t n_shared, int32_t H, int32_t I,
+                                  cle_dtype dt, void* ws, size_t ws_bytes,
+                                  void* const* phase_events, void* stream);
+
+/*
+ * cle_combine -- gate-weighted sum of each token's expert outputs (paper
+ * Eq. (1)), plus shared experts and the residual (paper §2.1,
+ * h_{l+1} = h'_l + MLP(h'_l)):
+ *   y[t] = round( sum_{s<k} gate[t,s] * yp[dest[t*k+s]]
+ *                 + sum_{q<n_shared} y_shared[q, t] + residual[t] ),
+ * accumulated in float32 in exactly that order; a slot with dest < 0
+ * contributes nothing.  y may alias residual (each element is read before
+ * it is written by the same thread); it must not overlap anything else.
+ *   y_shared [n_shared, T, H] or NULL; residual [T, H] or NULL.
+ * Requires H % 8 == 0.
+ */
+cle_status cle_combine(const void* yp, const int32_t* dest, const float* topk_gate,
+                       int32_t T, int32_t k, int32_t H,
+                       const void* y_shared, int32_t n_shared, const void* residual,
+                       void* y, cle_dtype dt, void* stream);
+
+/*
+ * cle_workload_stats -- per-group workloads and their step statistics.
+ * Paper §2.3, Eq. (2) and Eq. (3); the even expert-device mapping (Figure 1)
+ * gives group d the experts [d*E/D, (d+1)*E/D).
+ *
+ *   counts [n, E] int32: row j = counts of micro-batch j.
+ *   w      [n, D] int32 out: w[j][d] = sum of counts[j][e] over group d.
+ *   acc    [4] int64, accumulated only when runset_mask != 0 (may then not
+ *          be NULL).  With W_d = sum_{j in mask} w[j][d]:
+ *            acc[0] += sum_d W_d            (work done)
+ *            acc[1] += max_d W_d            (effective workload, Eq. (2))
+ *            acc[2] += sum_{j in mask} max_d w[j][d]  (the same work run alone)
+ *            acc[3] += 1                    (steps)
+ *          u = acc[0] / (D * acc[1]) is Eq. (3) over the accumulated steps.
+ * Requires 1 <= n <= 64, 1 <= D, E % D == 0, n*D <= 8192, mask bits < n.
+ */
+cle_status cle_workload_stats(const int32_t* counts, int32_t n, int32_t E, int32_t D,
+                              uint64_t runset_mask, int32_t* w, int64_t* acc, void* stream);
+
+/*
+ * cle_schedule_step -- Schedule(S, m) of Algorithm 1 (paper §4.2; policies
+ * §5.2).  Synchronous, pure host code; touches no device.
+ *
+ *   w          HOST [n, D] int32 workloads (row j = micro-batch j).
+ *   ready_mask bit j set = micro-batch j is in the pool S.
+ *   m          minimum RunSet size (1 <= m <= n); if |S| < m all of S runs.
+ *   runset_mask HOST out.
+ * With U(R) = sum_d W_d / (D * max_d W_d) of the combined workload (0 when
+ * it is all zero), compared exactly by cross-multiplication:
+ *   B0_ALONE    lowest ready id (m ignored);
+ *   B1_LOCKSTEP all of S (m ignored);
+ *   CUMUTIL     scan ready ids ascending, take the first, add a later id iff
+ *               U rises strictly; then pad to m with the lowest rejected ids;
+ *   MAXUTIL     argmax of U over subsets R of S with |R| >= m; ties to the
+ *               larger |R|, then to the lexicographically smallest sorted ids;
+ *               |S| <= CLE_MAX_MAXUTIL_POOL;
+ *   DIFFPEAK    scan ascending, take the first, add an id iff its peak group
+ *               (lowest index among maxima) is not a chosen id's peak; pad to m.
+ * Requires 1 <= n <= 64, D >= 1, ready_mask != 0 with bits < n.
+ */
+cle_status cle_schedule_step(const int32_t* w, int32_t n, int32_t D, uint64_t ready_mask,
+                             int32_t m, int32_t policy, uint64_t* runset_mask);
+
+/*
+ * cle_workspace_bytes -- device workspace, in bytes, that `op` needs:
+ *   CLE_OP_DISPATCH: depends on T, E, k (n_shared, n_desc ignored);
+ *   CLE_OP_FFN:      depends on E, n_shared, n_desc (T, k ignored).
+ * The workspace must be 256-byte aligned.  Returns 0 for an unknown op or
+ * out-of-range sizes.
+ */
+size_t cle_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t k, int32_t n_shared,
+                           int32_t n_desc);
+
+/* Static string for a status code. */
+const char* cle_status_string(cle_status s);
+
+/* Library version, "major.minor.patch". */
+const char* cle_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CLE_H */

@@ -1,0 +1,128 @@
+"""CPU-side checks of libcle.so: it loads, exports every symbol the header
+declares, validates arguments on the host, and its host scheduler matches the
+oracle bit for bit.  No GPU compute is issued here."""
+import json
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import cross_layer_expert_amd as cle
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cle.h")
+
+
+def test_every_declared_symbol_is_exported():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:cle_status|size_t|const char\*)\s+(cle_\w+)\s*\(", text,
+                              re.M))
+    assert {"cle_route", "cle_dispatch", "cle_grouped_expert_ffn", "cle_combine",
+            "cle_workload_stats", "cle_schedule_step", "cle_workspace_bytes"} <= declared
+    for name in declared:
+        assert hasattr(cle._lib, name), name
+    assert cle.version().count(".") == 2
+
+
+def test_status_strings():
+    for s in (cle.OK, cle.EINVAL, cle.EHIP, cle.EWORKSPACE, cle.EUNSUPPORTED):
+        assert cle.status_string(s)
+    assert cle.status_string(123) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert cle.workspace_bytes(cle.OP_DISPATCH, 2048, 128, 8) == 16 * 128 * 4
+    assert cle.workspace_bytes(cle.OP_DISPATCH, 0, 8, 2) == 256
+    assert cle.workspace_bytes(cle.OP_DISPATCH, 10, 2000, 2) == 0
+    b = cle.workspace_bytes(cle.OP_FFN, 0, 128, 1, 0, 4)
+    assert b >= 256 + 4 * 128 * 56 and b % 256 == 0
+    assert cle.workspace_bytes(cle.OP_FFN, 0, 64, 1, 2, 65) == 0
+    assert cle.workspace_bytes(99, 1, 1, 1) == 0
+
+
+def test_invalid_arguments_rejected_on_host():
+    """Each call fails validation before any HIP call (null device pointers
+    are never dereferenced)."""
+    L = cle._lib
+    assert L.cle_route(None, 4, 8, 9, None, None, None) == cle.EINVAL     # k > E
+    assert L.cle_route(None, 4, 2000, 1, None, None, None) == cle.EINVAL  # E > max
+    assert L.cle_route(None, 0, 8, 2, None, None, None) == cle.OK         # T == 0: nothing to do
+    assert L.cle_dispatch(None, 4, 2, 8, None, 12, 0, None, None, None, None, None, None, 0,
+                          None) == cle.EINVAL                              # H % 8
+    assert L.cle_combine(None, None, None, 4, 2, 64, None, 0, None, None, 7, None) == cle.EINVAL
+    assert L.cle_workload_stats(None, 2, 8, 3, 0, None, None, None) == cle.EINVAL
+    assert L.cle_workload_stats(8, 2, 8, 3, 0, 8, None, None) == cle.EINVAL  # E % D
+    assert L.cle_workload_stats(8, 2, 8, 4, 0b100, 8, 8, None) == cle.EINVAL  # mask bit >= n
+    d = (cle.FfnDesc * 1)(cle.FfnDesc(0, 8, 16, 16, 16, 16, 0, None, None, None))
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 96, 64, 1, None, 0,
+                                    None, None) == cle.EINVAL              # f32: H % 64
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 64, 64, 0, None, 0,
+                                    None, None) == cle.EINVAL              # bf16: H % 128
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, None, 0,
+                                    None, None) == cle.EWORKSPACE
+    d[0].layer = 2
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, None, 0,
+                                    None, None) == cle.EINVAL              # layer >= L
+
+
+def test_schedule_step_errors():
+    w = np.ones((4, 2), np.int32)
+    with pytest.raises(cle.CleError):
+        cle.schedule_step(w, 0, 1, cle.POLICY_CUMUTIL)          # empty pool
+    with pytest.raises(cle.CleError):
+        cle.schedule_step(w, 0b10000, 1, cle.POLICY_CUMUTIL)    # bit >= n
+    with pytest.raises(cle.CleError):
+        cle.schedule_step(w, 0b1111, 0, cle.POLICY_CUMUTIL)     # m < 1
+    with pytest.raises(cle.CleError):
+        cle.schedule_step(w, 0b1111, 5, cle.POLICY_CUMUTIL)     # m > n
+    with pytest.raises(cle.CleError):
+        cle.schedule_step(w, 0b1111, 1, 9)                       # policy
+    with pytest.raises(cle.CleError):
+        cle.schedule_step(-w, 0b1111, 1, cle.POLICY_B1_LOCKSTEP)  # negative workload
+    big = np.ones((24, 2), np.int32)
+    with pytest.raises(cle.CleError) as e:
+        cle.schedule_step(big, (1 << 24) - 1, 2, cle.POLICY_MAXUTIL)
+    assert e.value.status == cle.EUNSUPPORTED
+    # a pool smaller than m never needs the exhaustive search
+    assert cle.schedule_step(big, (1 << 24) - 1, 24, cle.POLICY_MAXUTIL) == (1 << 24) - 1
+
+
+def test_schedule_hand_examples():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "schedule_examples.json")))
+    for ex in g["examples"]:
+        w = np.array(ex["w"], np.int32)
+        ready = ex.get("ready", list(range(len(w))))
+        for name, want in ex["expect"].items():
+            got = cle.schedule_step(w, cle.mask_of(ready), ex["m"], cle.POLICIES[name])
+            assert cle.ids_of(got) == want, (ex["name"], name)
+
+
+@pytest.mark.parametrize("policy", ["b0", "b1", "cumutil", "maxutil", "diffpeak"])
+def test_schedule_matches_oracle_random(policy):
+    rnd = random.Random(hash(policy) & 0xffff)
+    for trial in range(400):
+        n = rnd.randint(1, 12 if policy == "maxutil" else 40)
+        D = rnd.randint(1, 9)
+        hot = rnd.random() < 0.5
+        w = np.array([[rnd.randint(0, 50) if not hot or rnd.random() < 0.3 else rnd.randint(0, 3)
+                       for _ in range(D)] for _ in range(n)], np.int32)
+        if rnd.random() < 0.1:
+            w[rnd.randrange(n)] = 0            # an empty micro-batch
+        ready = [j for j in range(n) if rnd.random() < 0.7] or [rnd.randrange(n)]
+        m = rnd.randint(1, n)
+        got = cle.ids_of(cle.schedule_step(w, cle.mask_of(ready), m, cle.POLICIES[policy]))
+        want = list(oracle.schedule([list(r) for r in w], ready, m, oracle.POLICIES[policy]))
+        assert got == want, (trial, w.tolist(), ready, m)
+
+
+def test_maxutil_large_pool_matches_oracle():
+    rnd = random.Random(5)
+    for _ in range(3):
+        n, D = 16, 8
+        w = np.array([[rnd.randint(0, 300) for _ in range(D)] for _ in range(n)], np.int32)
+        got = cle.ids_of(cle.schedule_step(w, (1 << n) - 1, 12, cle.POLICY_MAXUTIL))
+        want = list(oracle.schedule([list(r) for r in w], range(n), 12, oracle.POLICIES["maxutil"]))
+        assert got == want

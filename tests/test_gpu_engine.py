@@ -1,0 +1,139 @@
+"""GPU runs of Algorithm 1 through libcle.
+
+* tiny stack (fp32): schedule trace, u statistics and final hidden states
+  against the oracle's Algorithm 1, for every policy and m;
+* tiny stack: every (state, RunSet) transition of the (l_0, l_1, l_2) state
+  lattice -- the 699,121 schedules at m=1 pass only through these -- gives
+  bitwise the layer-by-layer outputs;
+* reduced Qwen3-shaped stack (bf16): every policy's final hidden states are
+  bitwise equal to the layer-by-layer (B0) run, and a sampled token chain
+  matches the oracle within the bf16 drift bound.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import cross_layer_expert_amd as cle
+import oracle
+import synth
+from cross_layer_expert_amd.engine import Engine
+from gpu_helpers import bits_of, check_close, device, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.CONFIGS["tiny"]
+
+
+def _tiny_setup(seed=0):
+    dev = device()
+    cfg = TINY
+    w13, w2, _, _ = synth.weights_numpy(cfg, seed)
+    logits = np.stack([np.stack([synth.logits(cfg, seed, j, l) for l in range(cfg.L)])
+                       for j in range(cfg.n)])
+    h0 = np.stack([synth.hidden(cfg, seed, j) for j in range(cfg.n)])
+    dev_in = ((to_dev(w13, "f32", dev), to_dev(w2, "f32", dev), None, None),
+              torch.from_numpy(logits).to(dev), to_dev(h0, "f32", dev))
+    host_in = (oracle.widen(w13, "f32"), oracle.widen(w2, "f32"), logits,
+               [oracle.widen(h, "f32") for h in h0])
+    return dev_in, host_in
+
+
+@pytest.mark.parametrize("policy", ["b0", "b1", "cumutil", "maxutil", "diffpeak"])
+@pytest.mark.parametrize("m", [1, 2, 3])
+def test_tiny_engine_matches_oracle(policy, m):
+    (W, logits_t, h0_t), (w13, w2, logits, h0) = _tiny_setup()
+    eng = Engine(W, logits_t, h0_t, TINY.D, TINY.k, cle.POLICIES[policy], m).run()
+    torch.cuda.synchronize()
+    h_ref, trace, acc, u = oracle.run_engine(h0, lambda j, l: logits[j, l], TINY.k, TINY.D,
+                                             w13, w2, m, oracle.POLICIES[policy])
+    assert eng.trace == trace, "schedule differs from the oracle's Algorithm 1"
+    a, ug = eng.stats()
+    assert a[:3] == list(acc) and a[3] == len(trace)
+    assert abs(ug - float(u)) < 1e-12
+    for j in range(TINY.n):
+        check_close(to_host(eng.h[j]), h_ref[j], 1e-5, 1e-5, what=f"h[{j}] {policy} m={m}")
+
+
+def test_tiny_state_lattice_bitwise():
+    """Every transition of the state lattice reproduces the canonical
+    per-(micro-batch, layer) outputs bit for bit."""
+    (W, logits_t, h0_t), _ = _tiny_setup(1)
+    n, L = TINY.n, TINY.L
+    eng = Engine(W, logits_t, h0_t, TINY.D, TINY.k, cle.POLICY_B0_ALONE, 1)
+    hist = {(j, 0): eng.h[j].clone() for j in range(n)}
+    while not eng.done:
+        R = eng.step()
+        for j in R:
+            hist[(j, eng.l[j])] = eng.h[j].clone()
+    torch.cuda.synchronize()
+    hist_bits = {key: bits_of(v) for key, v in hist.items()}
+    count = 0
+    for state in itertools.product(range(L + 1), repeat=n):
+        live = [j for j in range(n) if state[j] < L]
+        for r in range(1, len(live) + 1):
+            for R in itertools.combinations(live, r):
+                eng.l = list(state)
+                for j in R:
+                    eng.h[j].copy_(hist[(j, state[j])])
+                    eng.route_dispatch(j)
+                eng.moe_compute_combine(list(R))
+                for j in R:
+                    got = bits_of(eng.h[j])
+                    assert np.array_equal(got, hist_bits[(j, state[j] + 1)]), (state, R, j)
+                count += 1
+    print(f"[lattice] {count} transitions checked", flush=True)
+    assert count == sum(
+        (2 ** sum(1 for x in s if x < L) - 1) for s in itertools.product(range(L + 1), repeat=n))
+
+
+def _qwen_small(seed=0, L=6, T=256, n=4):
+    cfg = synth.small(synth.CONFIGS["qwen3"], L=L, T=T, n=n)
+    dev = device()
+    W = synth.weights_torch(cfg, seed, dev)
+    logits = np.stack([np.stack([synth.logits(cfg, seed, j, l) for l in range(cfg.L)])
+                       for j in range(cfg.n)])
+    h0 = np.stack([synth.hidden(cfg, seed, j) for j in range(cfg.n)])
+    return cfg, W, logits, h0
+
+
+def test_qwen3_shaped_cross_layer_equals_layer_by_layer():
+    cfg, W, logits, h0 = _qwen_small()
+    dev = device()
+    lt, ht = torch.from_numpy(logits).to(dev), to_dev(h0, "bf16", dev)
+    base = Engine(W, lt, ht, cfg.D, cfg.k, cle.POLICY_B0_ALONE, 1).run()
+    ref = bits_of(base.h)
+    acc0, u0 = base.stats()
+    for policy in ("cumutil", "maxutil", "diffpeak", "b1"):
+        eng = Engine(W, lt, ht, cfg.D, cfg.k, cle.POLICIES[policy], cfg.m).run()
+        assert np.array_equal(bits_of(eng.h), ref), policy
+        acc, u = eng.stats()
+        assert acc[0] == acc0[0] and u >= u0 - 1e-15
+        print(f"[qwen3-small] {policy}: steps={acc[3]} 1-u={1 - u:.4f} (B0 {1 - u0:.4f})",
+              flush=True)
+
+
+def test_qwen3_shaped_sampled_chain_vs_oracle():
+    """Three tokens of micro-batch 1 followed through all layers by the oracle
+    from the seeded inputs alone (a token's chain depends only on its own
+    row).  The GPU stores h in bf16 after every layer; the bound allows that
+    rounding to accumulate over L layers."""
+    cfg, W, logits, h0 = _qwen_small(L=4, T=128, n=2)
+    dev = device()
+    eng = Engine(W, torch.from_numpy(logits).to(dev), to_dev(h0, "bf16", dev), cfg.D, cfg.k,
+                 cle.POLICY_CUMUTIL, 1).run()
+    got = oracle.widen(to_host(eng.h[1]), "bf16")
+    w13, w2 = W[0], W[1]
+    for t in (0, 77, 127):
+        x = oracle.widen(h0[1, t:t + 1], "bf16")
+        for l in range(cfg.L):
+            idx, gates = oracle.route(logits[1, l, t:t + 1], cfg.k)
+            # each slot's expert output for this one token, then Eq. (1) + residual
+            yp = np.concatenate([
+                oracle.swiglu_expert(x, oracle.widen(to_host(w13[l, int(e)]), "bf16"),
+                                     oracle.widen(to_host(w2[l, int(e)]), "bf16"))
+                for e in idx[0]])
+            x = oracle.combine(yp, np.arange(cfg.k), gates, cfg.k, residual=x)
+        check_close(got[t:t + 1], x, 2e-2 * cfg.L ** 0.5, 1e-2,
+                    what=f"token {t} after {cfg.L} layers")
