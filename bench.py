@@ -1,0 +1,338 @@
+"""Throughput of the cross-layer MoE step on one MI355X.
+
+A timed step is one iteration of Algorithm 1 of EasyBalance over the
+Qwen3-30B-A3B-shaped synthetic stack (48 layers, hidden 2048, 128 experts
+top-8, SwiGLU intermediate 768, D = 8 groups, 4 micro-batches of 2048
+tokens): route + dispatch of the previous RunSet, workload statistics, the
+host scheduler (CumUtil, m = 3), one grouped expert launch per GEMM phase for
+every RunSet member at its own layer, and the gate-weighted combine.  When all
+micro-batches have passed layer 48 the engine restarts at layer 0.
+
+Prints one JSON line (rank 0):
+  value      expert tokens/s over the timed steps (inputs resident in HBM);
+  roofline   the dominant kernel (grouped gate/up GEMM): algorithmic bytes or
+             FLOPs per launch / its mean launch time from HIP events recorded
+             on the library's stream during the timed steps;
+  cpu_baseline the CPU oracle on one (micro-batch, layer) unit of the same
+             workload, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "expert tokens/s per cross-layer MoE step; % bf16 MFMA peak; under-util 1-u"
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        st = self.lib.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        assert st == 0, st
+        return float(f.value)
+
+
+def workload_name(cfg) -> str:
+    s = (f"{cfg.name}-shaped MoE stack: {cfg.L} layers, hidden {cfg.H}, {cfg.E} experts top-{cfg.k}"
+         f", SwiGLU I {cfg.I}, D={cfg.D}, {cfg.n} micro-batches x {cfg.T} tokens")
+    if cfg.n_shared:
+        s += f", +{cfg.n_shared} shared experts"
+    if cfg.bias == "zipf":
+        s += f", Zipf({cfg.zipf_s}) skew"
+    if cfg.profiles > 1:
+        s += f", {cfg.profiles} skew profiles"
+    if cfg.start_layers:
+        s += ", staggered start layers 3j"
+    return s
+
+
+def setup(cfg, seed, dev):
+    import torch
+    import synth
+    t0 = time.time()
+    W = synth.weights_torch(cfg, seed, dev)
+    logits = np.stack([np.stack([synth.logits(cfg, seed, j, l) for l in range(cfg.L)])
+                       for j in range(cfg.n)])
+    lt = torch.from_numpy(logits).to(dev)
+    h0 = np.stack([synth.hidden(cfg, seed, j) for j in range(cfg.n)])
+    ht = torch.from_numpy(h0.view(np.int16)).to(dev).view(torch.bfloat16)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    return W, lt, ht, logits, h0
+
+
+def counts_of(eng, j, l):
+    """Per-expert counts of micro-batch j at layer l, from the library's route
+    and dispatch kernels (routing depends only on the logits)."""
+    import cross_layer_expert_amd as cle
+    saved = eng.l[j]
+    eng.l[j] = l
+    eng.route_dispatch(j)
+    eng.l[j] = saved
+    return eng.counts[j].clone()
+
+
+def ffn_work(cfg, members, counts_host):
+    """Algorithmic bytes and FLOPs of the two GEMM phases of one grouped launch.
+
+    members: list of (j, layer); counts_host[(j, layer)] = per-expert counts.
+    Weights of a distinct (layer, expert) are read once; activations once."""
+    H, I = cfg.H, cfg.I
+    touched = set()
+    rows = 0
+    for j, l in members:
+        c = counts_host[(j, l)]
+        rows += int(c.sum())
+        touched.update((l, int(e)) for e in np.flatnonzero(c))
+        if cfg.n_shared:
+            rows += cfg.n_shared * cfg.T
+            touched.update((l, -1 - q) for q in range(cfg.n_shared))
+    nw = len(touched)
+    b1 = nw * 2 * I * H * 2 + rows * (H * 2 + I * 2)
+    b2 = nw * H * I * 2 + rows * (I * 2 + H * 2)
+    f1 = 2.0 * rows * H * 2 * I
+    f2 = 2.0 * rows * I * H
+    return b1, b2, f1, f2
+
+
+def schedule_only_u(cfg, w_table, policy, m):
+    """1-u of Algorithm 1 over a full run, from the per-(micro-batch, layer)
+    workloads, with the library's host scheduler."""
+    import cross_layer_expert_amd as cle
+    n, L = cfg.n, cfg.L
+    lj = list(cfg.start_layers) if cfg.start_layers else [0] * n
+    S = [j for j in range(n) if lj[j] < L]
+    num = den = sep = steps = 0
+    while S:
+        w = np.zeros((n, cfg.D), np.int32)
+        for j in S:
+            w[j] = w_table[j][lj[j]]
+        R = cle.ids_of(cle.schedule_step(w, cle.mask_of(S), m, policy))
+        Wd = w[R].sum(axis=0)
+        num += int(Wd.sum())
+        den += int(Wd.max())
+        sep += int(w[R].max(axis=1).sum())
+        steps += 1
+        for j in R:
+            lj[j] += 1
+        S = [j for j in S if lj[j] < L]
+    return 1.0 - num / (cfg.D * den), steps, sep / den
+
+
+def cpu_baseline(cfg, W, logits, h0, budget_s):
+    """The CPU oracle on (micro-batch, layer) units of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    done_tok, spent, units = 0, 0.0, []
+    j = 0
+    for l in range(cfg.L):
+        w13 = oracle.widen(W[0][l].cpu().view(__import__("torch").int16).numpy().view(np.uint16),
+                           "bf16")
+        w2 = oracle.widen(W[1][l].cpu().view(__import__("torch").int16).numpy().view(np.uint16),
+                          "bf16")
+        x = oracle.widen(h0[j], "bf16")
+        t0 = time.perf_counter()
+        out = oracle.moe_layer(x, logits[j, l], cfg.k, w13, w2)
+        dt = time.perf_counter() - t0
+        assert np.isfinite(out["y"]).all()
+        spent += dt
+        done_tok += cfg.T * cfg.k
+        units.append((j, l))
+        del w13, w2
+        if spent >= budget_s:
+            break
+    return dict(value=done_tok / spent, unit="expert tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{len(units)} (micro-batch, layer) unit(s) of the {cfg.name} workload "
+                       f"(micro-batch 0, layers 0..{len(units) - 1}; {done_tok} expert tokens; "
+                       f"route, dispatch, float64 SwiGLU experts, combine); {spent:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--config", default="qwen3")
+    ap.add_argument("--policy", default="cumutil")
+    ap.add_argument("--m", type=int, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip whole-run and 1-u passes")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the expert-parallel sharding over "
+              "several GPUs is a design, not code (set --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import cross_layer_expert_amd as cle
+    import synth
+    from cross_layer_expert_amd.engine import Engine
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    m = args.m if args.m is not None else cfg.m
+    policy = cle.POLICIES[args.policy]
+    if cfg.start_layers and args.policy == "cumutil" and args.m is None:
+        policy, m = cle.POLICY_B1_LOCKSTEP, cfg.n     # decode: the staggered 16-layer step
+
+    if args.calib_copy:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    W, lt, ht, logits, h0 = setup(cfg, args.seed, dev)
+    stream = torch.cuda.current_stream()
+    eng = Engine(W, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
+                 stream=stream)
+    hip = HipEvents()
+
+    def one_step(events=None):
+        if eng.done:
+            eng.reset()
+        return eng.step(events=events)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [hip.create(3) for _ in range(K)]
+    steps = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        one_step(events=evs[i])
+        R, layers = eng.trace[-1]
+        steps.append(list(zip(R, layers)))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    tok = sum(len(R) * cfg.T * (cfg.k + cfg.n_shared) for R in steps)
+    value = tok / elapsed
+    g1 = [hip.ms(e[0], e[1]) for e in evs]
+    g2 = [hip.ms(e[1], e[2]) for e in evs]
+
+    # algorithmic work of every timed launch (counts recomputed by the library)
+    need = sorted({jl for R in steps for jl in R})
+    counts_host = {}
+    for (j, l) in need:
+        counts_host[(j, l)] = counts_of(eng, j, l).cpu().numpy()
+    B1 = B2 = F1 = F2 = 0.0
+    for R in steps:
+        b1, b2, f1, f2 = ffn_work(cfg, R, counts_host)
+        B1, B2, F1, F2 = B1 + b1, B2 + b2, F1 + f1, F2 + f2
+    t1, t2 = sum(g1) / 1e3, sum(g2) / 1e3
+    ai1 = F1 / B1
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai1 < ridge:
+        ach = B1 / K / (t1 / K) / 1e9
+        roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+    else:
+        ach = F1 / K / (t1 / K) / 1e12
+        roof = dict(bound="mfma", achieved=round(ach, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None)
+    roof.update(kernel="ffn_gemm_bf16<1> (grouped gate/up + SwiGLU)",
+                mean_launch_us=round(t1 / K * 1e6, 2),
+                algorithmic_bytes_per_launch=int(B1 / K), flops_per_launch=int(F1 / K))
+
+    gemm_tflops = (F1 + F2) / (t1 + t2) / 1e12
+    extras = dict(
+        gemm_tflops=round(gemm_tflops, 1),
+        mfma_peak_frac=round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+        gemm_hbm_frac=round((B1 + B2) / (t1 + t2) / 1e9 / HBM_PEAK_GBS, 4),
+        down_mean_launch_us=round(t2 / K * 1e6, 2),
+        ffn_share_of_step=round((t1 + t2) / elapsed, 3),
+    )
+
+    if not args.no_extras:
+        # per-(micro-batch, layer) workloads of the whole stack -> 1-u per policy
+        w_table = [[None] * cfg.L for _ in range(cfg.n)]
+        for j in range(cfg.n):
+            for l in range(cfg.L):
+                c = counts_of(eng, j, l).view(1, -1)
+                wd = torch.empty((1, cfg.D), dtype=torch.int32, device=dev)
+                cle.workload_stats(c, cfg.D, 0, wd)
+                w_table[j][l] = wd.cpu().numpy()[0]
+        uu = {}
+        for name in ("b0", "b1", "cumutil", "maxutil", "diffpeak"):
+            one_minus_u, nsteps, ratio = schedule_only_u(cfg, w_table, cle.POLICIES[name], m)
+            uu[name] = dict(one_minus_u=round(one_minus_u, 4), steps=nsteps)
+        extras["under_util"] = uu
+        # measured whole runs: cross-layer (timed policy) vs one (j, l) per step
+        runs = {}
+        for name, pol, mm in (("b0", cle.POLICY_B0_ALONE, 1), (args.policy, policy, m)):
+            e2 = Engine(W, lt, ht, cfg.D, cfg.k, pol, mm, start_layers=cfg.start_layers,
+                        stream=stream)
+            e2.step()
+            e2.reset()
+            torch.cuda.synchronize()
+            s0 = time.perf_counter()
+            e2.run()
+            torch.cuda.synchronize()
+            runs[name] = dict(ms=round((time.perf_counter() - s0) * 1e3, 2),
+                              steps=len(e2.trace), one_minus_u=round(1 - e2.stats()[1], 4))
+            del e2
+        extras["whole_run"] = runs
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, W, logits, h0, args.cpu_budget)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "expert tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded router logits with Zipf skew, N(0,1) hidden, N(0,0.02) weights)",
+        "config": {"workload": workload_name(cfg), "policy": args.policy if policy != 1 else "b1",
+                   "m": m, "seed": args.seed, "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    out.update(extras)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

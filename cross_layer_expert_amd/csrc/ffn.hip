@@ -29,10 +29,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 64;        // rows per tile (both phases, both dtypes)
-constexpr int kBN1 = 64;       // act columns per phase-1 tile
-constexpr int kBN2 = 128;      // output columns per phase-2 tile (bf16)
-constexpr int kBN2F = 64;      // output columns per phase-2 tile (f32)
+constexpr int kBM = 64;        // rows per tile of the f32 path
+constexpr int kBNF = 64;       // columns per tile of the f32 path (both phases)
 constexpr int kBK = 64;        // K per pipeline step
 constexpr int kPlanDescs = 16;
 constexpr int kXcds = 8;
@@ -56,7 +54,8 @@ struct PlanArgs {
   const void* w13s;
   const void* w2s;
   int nd, seg_base, first;
-  int E, ns, H, I, esz, bn2;
+  int E, ns, H, I, esz;
+  int tm, tn1, tn2;  // tile rows, phase-1 act columns, phase-2 output columns
 };
 
 // ---------------------------------------------------------------- planning
@@ -85,10 +84,10 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
   const int nseg = p.nd * (p.E + p.ns);
   const int per = (nseg + 1023) / 1024;
   const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
-  const int n1 = p.I / kBN1, n2 = p.H / p.bn2;
+  const int n1 = p.I / p.tn1, n2 = p.H / p.tn2;
   int c1 = 0, c2 = 0;
   for (int s = lo; s < hi; ++s) {
-    const int mt = (seg_rows(p, s) + kBM - 1) / kBM;
+    const int mt = (seg_rows(p, s) + p.tm - 1) / p.tm;
     c1 += mt * n1;
     c2 += mt * n2;
   }
@@ -138,7 +137,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
     g.t2 = t2;
     g.pad_ = 0;
     segs[p.seg_base + s] = g;
-    const int mt = (g.rows + kBM - 1) / kBM;
+    const int mt = (g.rows + p.tm - 1) / p.tm;
     t1 += mt * n1;
     t2 += mt * n2;
   }
@@ -174,119 +173,258 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // c ^ (r & 7) to spread the column reads of 16 rows over the banks.
 __device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
 
-template <int PHASE>
-__global__ __launch_bounds__(256) void ffn_gemm_bf16(const Seg* __restrict__ segs, int nseg,
-                                                     const int* __restrict__ totals, int H,
-                                                     int I) {
-  __shared__ uint4 a_lds[2][kBM * 8];
+// Workgroup barrier for LDS hand-off only.  __syncthreads() also orders
+// global memory, which on gfx9 means waiting for every outstanding vector
+// load -- including the prefetches of later K steps -- so it would drain the
+// software pipeline at every step.  Here only LDS traffic is waited for.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16-byte load from global memory.  The pointers come out of the segment
+// table, so the compiler cannot see their address space and would emit flat
+// loads, which also count against the LDS counter and would make every
+// LDS barrier wait for the prefetches; the cast makes them global loads.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+  const u32x4 v = *(gu32x4*)(p);
+  return __builtin_bit_cast(uint4, v);
+}
+
+// Grouped GEMM tile kernel (bf16, gfx950).
+//
+// The kernel is bound by how many cache-line requests each CU keeps in
+// flight, so (a) the tile is as large as the accumulators allow, cutting the
+// re-reads of weights (once per row tile) and activations (once per column
+// tile), and (b) operands are moved with direct global->LDS loads
+// (global_load_lds_dwordx4), which need no registers, into a kStages-deep
+// ring of LDS stages, so kStages-1 K steps are in flight during each MFMA
+// step.
+//
+// Tile: kTM = 128 rows x WN wavefronts; wavefront w owns two 16-row weight
+// blocks (phase 1: the gate rows and the up rows of 16 act columns; phase 2:
+// 32 output columns) and computes all kTM rows of them.  Every direct load
+// instruction moves one 16 x 32 bf16 MFMA operand fragment (1 KiB); lane l's
+// 16 bytes land at byte 16*l of the fragment slot, which is exactly where the
+// MFMA operand read of lane l expects them, so LDS reads are contiguous and
+// conflict-free.  Row blocks past the end of a segment are skipped (no
+// loads, no MFMAs, no stores).
+constexpr int kTM = 128;
+constexpr int kMB = kTM / 16;   // 16-row blocks per tile
+constexpr int kStages = 3;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gvoid;
+
+__device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_slot) {
+  __builtin_amdgcn_global_load_lds((gvoid*)(src), (lds_void*)(lds_slot), 16, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Barrier once this wavefront's LDS reads have completed; the empty asm keeps
+// the compiler from moving LDS reads above it.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kMaxWN = 8;
+
+// One pipeline stage: the operand fragments of one K step of a tile.
+struct StageLDS {
+  uint4 w[kMaxWN * 4][64];  // [wave*4 + block*2 + half][lane]
+  uint4 x[kMB * 2][64];     // [rowblock*2 + half][lane]
+};
+// Three stages, referenced by name (one set per kernel instantiation), so the
+// compiler can tell which stage each direct load writes and each read reads,
+// and waits only for the loads a read depends on.
+template <int PHASE, int WN>
+__shared__ StageLDS g_st0;
+template <int PHASE, int WN>
+__shared__ StageLDS g_st1;
+template <int PHASE, int WN>
+__shared__ StageLDS g_st2;
+
+// Everything one tile needs, resolved from the segment table.
+struct TileArgs {
+  const uint16_t* w0p;  // this lane's first weight row (+ its K offset)
+  const uint16_t* w1p;  // this lane's second weight row
+  const uint16_t* A;    // first row of the tile's A operand
+  uint16_t* out;        // first row of the tile's output
+  int K;                // reduction length (row stride of A and W)
+  int ldo;              // output row stride
+  int col;              // this lane's first output column
+  int nrows;            // valid rows of the tile (1..kTM)
+};
+
+// The K loop and epilogue of one tile with NMB active 16-row blocks (a
+// compile-time count, so the MFMA sequence has no data-dependent branches).
+template <int PHASE, int WN, int NMB>
+__device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) {
+  constexpr int XB = kMB / WN;  // x row blocks owned by each wavefront
+  const int l16 = lane % 16, g4 = lane / 16;
+  const int KT = t.K / kBK;
+  // x fragments this wavefront loads; rows past the tile are clamped to its
+  // last row (cheap repeated reads; those output rows are never stored)
+  const uint16_t* xp[XB];
+#pragma unroll
+  for (int b = 0; b < XB; ++b) {
+    const int mb = wave * XB + b;
+    xp[b] = t.A + min(mb * 16 + l16, t.nrows - 1) * t.K + g4 * 8;
+  }
+  f32x4 acc0[NMB], acc1[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    acc0[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // request K step KT_ into stage ST
+#define CLE_ISSUE(ST, KT_)                                                          \
+  {                                                                                 \
+    const int ko = (KT_) * kBK;                                                     \
+    dma16(t.w0p + ko, &ST.w[wave * 4 + 0][0]);                                      \
+    dma16(t.w0p + ko + 32, &ST.w[wave * 4 + 1][0]);                                 \
+    dma16(t.w1p + ko, &ST.w[wave * 4 + 2][0]);                                      \
+    dma16(t.w1p + ko + 32, &ST.w[wave * 4 + 3][0]);                                 \
+    _Pragma("unroll") for (int b = 0; b < XB; ++b) {                                \
+      dma16(xp[b] + ko, &ST.x[(wave * XB + b) * 2 + 0][0]);                         \
+      dma16(xp[b] + ko + 32, &ST.x[(wave * XB + b) * 2 + 1][0]);                    \
+    }                                                                               \
+  }
+  // K half outer, row block inner: every accumulator sees the two halves of
+  // a K step in the same order in every tile shape
+#define CLE_COMPUTE(ST)                                                             \
+  _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                   \
+    const bf16x8 B0 = __builtin_bit_cast(bf16x8, ST.w[wave * 4 + h][lane]);         \
+    const bf16x8 B1 = __builtin_bit_cast(bf16x8, ST.w[wave * 4 + 2 + h][lane]);     \
+    _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb) {                            \
+      const bf16x8 Af = __builtin_bit_cast(bf16x8, ST.x[mb * 2 + h][lane]);         \
+      acc0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B0, acc0[mb], 0, 0, 0); \
+      acc1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B1, acc1[mb], 0, 0, 0); \
+    }                                                                               \
+  }
+  // Step KT_ (in stage CUR): wait for this wavefront's loads of step KT_ (the
+  // loads of step KT_+1 may stay in flight), barrier (every wavefront's loads
+  // of step KT_ have landed and every wavefront is done with step KT_-1),
+  // request step KT_+2 into the stage of step KT_-1, compute.  Requests are
+  // unconditional (the step index is clamped at the end, re-reading the last
+  // step into a finished stage) so that every wavefront has exactly
+  // kPerStep requests per step in flight and the compiler can track which
+  // stage each request writes.
+  constexpr int kPerStep = 4 + 2 * XB;
+#define CLE_STEP(CUR, NXT2, KT_)                                                    \
+  {                                                                                 \
+    wait_vmcnt<kPerStep>();                                                         \
+    stage_barrier();                                                                \
+    CLE_ISSUE(NXT2, min((KT_) + 2, KT - 1));                                        \
+    CLE_COMPUTE(CUR);                                                               \
+  }
+
+  auto& st0 = g_st0<PHASE, WN>;
+  auto& st1 = g_st1<PHASE, WN>;
+  auto& st2 = g_st2<PHASE, WN>;
+  CLE_ISSUE(st0, 0);
+  CLE_ISSUE(st1, min(1, KT - 1));
+  int kt = 0;
+  for (; kt + 3 <= KT; kt += 3) {
+    CLE_STEP(st0, st2, kt);
+    CLE_STEP(st1, st0, kt + 1);
+    CLE_STEP(st2, st1, kt + 2);
+  }
+  if (kt < KT) {
+    CLE_STEP(st0, st2, kt);
+    ++kt;
+  }
+  if (kt < KT) {
+    CLE_STEP(st1, st0, kt);
+  }
+#undef CLE_ISSUE
+#undef CLE_COMPUTE
+#undef CLE_STEP
+  wait_vmcnt<0>();  // the clamped tail requests have landed before stages are reused
+
+  // epilogue: lane holds rows mb*16 + g4*4 + i, column l16 of each block
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = mb * 16 + g4 * 4 + i;
+      if (row < t.nrows) {
+        if (PHASE == 1) {
+          t.out[row * t.ldo + t.col] = f32_to_bf16(silu(acc0[mb][i]) * acc1[mb][i]);
+        } else {
+          t.out[row * t.ldo + t.col] = f32_to_bf16(acc0[mb][i]);
+          t.out[row * t.ldo + t.col + 16] = f32_to_bf16(acc1[mb][i]);
+        }
+      }
+    }
+  }
+}
+
+template <int PHASE, int WN>
+__global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restrict__ segs,
+                                                            int nseg,
+                                                            const int* __restrict__ totals,
+                                                            int H, int I) {
+  static_assert(kMB % WN == 0 && WN <= kMaxWN, "wavefronts per tile");
   const int total = totals[PHASE - 1];
   const int grid = gridDim.x;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int l16 = lane % 16, g4 = lane / 16;
-  const int K = PHASE == 1 ? H : I;                 // reduction length = row stride of A and W
-  const int KT = K / kBK;
-  // A staging: thread -> (row, 32-byte quarter)
-  const int ar = threadIdx.x / 4, aq = threadIdx.x % 4;
+  const int K = PHASE == 1 ? H : I;
 
   for (int tile = logical_tile_base(grid); tile < total; tile += grid) {
     const int si = find_seg<PHASE>(segs, nseg, tile);
     const Seg sg = segs[si];
-    const int mt = (sg.rows + kBM - 1) / kBM;
+    const int mt = (sg.rows + kTM - 1) / kTM;
     const int r = tile - (PHASE == 1 ? sg.t1 : sg.t2);
     const int nt = r / mt, mi = r % mt;
-    const int row0 = mi * kBM;
-    const uint16_t* A = PHASE == 1 ? sg.a : static_cast<const uint16_t*>(sg.act);
+    const int row0 = mi * kTM;
+    TileArgs t;
+    t.K = K;
+    t.nrows = min(kTM, sg.rows - row0);
+    t.A = (PHASE == 1 ? sg.a : static_cast<const uint16_t*>(sg.act)) +
+          static_cast<int64_t>(row0) * K;
     const uint16_t* W = static_cast<const uint16_t*>(PHASE == 1 ? sg.w13 : sg.w2);
-    // this lane's two weight rows (operand B of the two MFMA column blocks)
     int wrow0, wrow1;
     if (PHASE == 1) {
-      wrow0 = nt * kBN1 + wave * 16 + l16;  // gate row
-      wrow1 = I + wrow0;                    // up row of the same act column
+      wrow0 = nt * (16 * WN) + wave * 16 + l16;  // gate row
+      wrow1 = I + wrow0;                         // up row of the same act column
+      t.out = static_cast<uint16_t*>(sg.act) + static_cast<int64_t>(row0) * I;
+      t.ldo = I;
+      t.col = nt * (16 * WN) + wave * 16 + l16;
     } else {
-      wrow0 = nt * kBN2 + wave * 32 + l16;
+      wrow0 = nt * (32 * WN) + wave * 32 + l16;
       wrow1 = wrow0 + 16;
+      t.out = static_cast<uint16_t*>(sg.y) + static_cast<int64_t>(row0) * H;
+      t.ldo = H;
+      t.col = nt * (32 * WN) + wave * 32 + l16;
     }
-    const uint16_t* w0p = W + static_cast<int64_t>(wrow0) * K + g4 * 8;
-    const uint16_t* w1p = W + static_cast<int64_t>(wrow1) * K + g4 * 8;
-    // Rows past the segment end load the last valid row instead: an MFMA
-    // output row depends only on its own A row, and those rows are never
-    // stored, so no masking is needed.
-    const int arow = min(row0 + ar, sg.rows - 1);
-    const uint16_t* ap = A + static_cast<int64_t>(arow) * K + aq * 16;
-
-    f32x4 acc0[4], acc1[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      acc0[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    t.w0p = W + static_cast<int64_t>(wrow0) * K + g4 * 8;
+    t.w1p = W + static_cast<int64_t>(wrow1) * K + g4 * 8;
+    switch ((t.nrows + 15) / 16) {
+      case 1: tile_nmb<PHASE, WN, 1>(t, wave, lane); break;
+      case 2: tile_nmb<PHASE, WN, 2>(t, wave, lane); break;
+      case 3: tile_nmb<PHASE, WN, 3>(t, wave, lane); break;
+      case 4: tile_nmb<PHASE, WN, 4>(t, wave, lane); break;
+      case 5: tile_nmb<PHASE, WN, 5>(t, wave, lane); break;
+      case 6: tile_nmb<PHASE, WN, 6>(t, wave, lane); break;
+      case 7: tile_nmb<PHASE, WN, 7>(t, wave, lane); break;
+      default: tile_nmb<PHASE, WN, 8>(t, wave, lane); break;
     }
-    uint4 b00 = *reinterpret_cast<const uint4*>(w0p);
-    uint4 b01 = *reinterpret_cast<const uint4*>(w0p + 32);
-    uint4 b10 = *reinterpret_cast<const uint4*>(w1p);
-    uint4 b11 = *reinterpret_cast<const uint4*>(w1p + 32);
-    a_lds[0][a_slot(ar, 2 * aq)] = *reinterpret_cast<const uint4*>(ap);
-    a_lds[0][a_slot(ar, 2 * aq + 1)] = *reinterpret_cast<const uint4*>(ap + 8);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      // prefetch step kt+1 (the last step re-reads itself; never consumed)
-      const int ko = min(kt + 1, KT - 1) * kBK;
-      const uint4 na0 = *reinterpret_cast<const uint4*>(ap + ko);
-      const uint4 na1 = *reinterpret_cast<const uint4*>(ap + ko + 8);
-      const uint4 n00 = *reinterpret_cast<const uint4*>(w0p + ko);
-      const uint4 n01 = *reinterpret_cast<const uint4*>(w0p + ko + 32);
-      const uint4 n10 = *reinterpret_cast<const uint4*>(w1p + ko);
-      const uint4 n11 = *reinterpret_cast<const uint4*>(w1p + ko + 32);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 B0 = __builtin_bit_cast(bf16x8, s == 0 ? b00 : b01);
-        const bf16x8 B1 = __builtin_bit_cast(bf16x8, s == 0 ? b10 : b11);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const bf16x8 Af =
-              __builtin_bit_cast(bf16x8, a_lds[cur][a_slot(mb * 16 + l16, s * 4 + g4)]);
-          acc0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B0, acc0[mb], 0, 0, 0);
-          acc1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B1, acc1[mb], 0, 0, 0);
-        }
-      }
-      // buffer cur^1 was last read before the previous barrier
-      a_lds[cur ^ 1][a_slot(ar, 2 * aq)] = na0;
-      a_lds[cur ^ 1][a_slot(ar, 2 * aq + 1)] = na1;
-      b00 = n00;
-      b01 = n01;
-      b10 = n10;
-      b11 = n11;
-      __syncthreads();
-    }
-
-    // epilogue: lane holds rows mb*16 + g4*4 + i, column l16 of each block
-    if (PHASE == 1) {
-      uint16_t* out = static_cast<uint16_t*>(sg.act);
-      const int col = nt * kBN1 + wave * 16 + l16;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = row0 + mb * 16 + g4 * 4 + i;
-          if (row < sg.rows)
-            out[static_cast<int64_t>(row) * I + col] = f32_to_bf16(silu(acc0[mb][i]) * acc1[mb][i]);
-        }
-    } else {
-      uint16_t* out = static_cast<uint16_t*>(sg.y);
-      const int col = nt * kBN2 + wave * 32 + l16;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = row0 + mb * 16 + g4 * 4 + i;
-          if (row < sg.rows) {
-            out[static_cast<int64_t>(row) * H + col] = f32_to_bf16(acc0[mb][i]);
-            out[static_cast<int64_t>(row) * H + col + 16] = f32_to_bf16(acc1[mb][i]);
-          }
-        }
-    }
+    // every wavefront is done reading the stages before the next tile's
+    // first requests overwrite them
+    stage_barrier();
   }
 }
 
@@ -329,8 +467,22 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const Seg* __restrict__ segs
   }
 }
 
-int persistent_grid(int64_t upper_bound_tiles) {
-  int64_t g = static_cast<int64_t>(device_cu_count()) * 4;
+// Workgroups that fit on the device at once for `kernel` (cached per device).
+template <typename Kernel>
+int resident_blocks(Kernel kernel, int* cache, int threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] > 0) return cache[dev];
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  cache[dev] = per_cu * device_cu_count();
+  return cache[dev];
+}
+
+int persistent_grid(int64_t upper_bound_tiles, int resident) {
+  int64_t g = resident;
   if (upper_bound_tiles < g) g = upper_bound_tiles;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return static_cast<int>(g);
@@ -349,8 +501,14 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
   if (!d || n_desc < 1 || n_desc > CLE_MAX_DESC) return CLE_EINVAL;
   if (!w13 || !w2 || L < 1 || E < 1 || E > CLE_MAX_E || n_shared < 0) return CLE_EINVAL;
   if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
-  const int bn2 = dt == CLE_BF16 ? kBN2 : kBN2F;
-  if (H < bn2 || H % bn2 || I < kBN1 || I % kBN1) return CLE_EINVAL;
+  // bf16: 256-row tiles of WN wavefronts (16*WN act columns, 32*WN output
+  // columns); WN = 8 when the shape allows it, else 4.  f32: 64 x 64 tiles.
+  if (I < 64 || I % 64) return CLE_EINVAL;
+  if (dt == CLE_BF16 ? (H < 128 || H % 128) : (H < 64 || H % 64)) return CLE_EINVAL;
+  const int wn = (dt == CLE_BF16 && I % 128 == 0 && H % 256 == 0) ? 8 : 4;
+  const int tm = dt == CLE_BF16 ? kTM : kBM;
+  const int tn1 = dt == CLE_BF16 ? 16 * wn : kBNF;
+  const int tn2 = dt == CLE_BF16 ? 32 * wn : kBNF;
   if (n_shared > 0 && (!w13_shared || !w2_shared)) return CLE_EINVAL;
   const int esz = dt == CLE_BF16 ? 2 : 4;
   if (!aligned(w13, 16) || !aligned(w2, 16)) return CLE_EINVAL;
@@ -367,10 +525,11 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
         return CLE_EINVAL;
     }
     // sum over experts of ceil(c_e / BM) <= rows / BM + (non-empty experts)
-    const int64_t mt = q.rows / kBM + (q.rows < E ? q.rows : E);
-    const int64_t mts = n_shared > 0 ? static_cast<int64_t>(n_shared) * ((q.shared_rows + kBM - 1) / kBM) : 0;
-    ub1 += (mt + mts) * (I / kBN1);
-    ub2 += (mt + mts) * (H / bn2);
+    const int64_t mt = q.rows / tm + (q.rows < E ? q.rows : E);
+    const int64_t mts =
+        n_shared > 0 ? static_cast<int64_t>(n_shared) * ((q.shared_rows + tm - 1) / tm) : 0;
+    ub1 += (mt + mts) * (I / tn1);
+    ub2 += (mt + mts) * (H / tn2);
   }
   if (ub1 > INT32_MAX || ub2 > INT32_MAX) return CLE_EUNSUPPORTED;
   const size_t need = cle_workspace_bytes(CLE_OP_FFN, 0, E, 1, n_shared, n_desc);
@@ -399,26 +558,39 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
     p.H = H;
     p.I = I;
     p.esz = esz;
-    p.bn2 = bn2;
+    p.tm = tm;
+    p.tn1 = tn1;
+    p.tn2 = tn2;
     ffn_plan<<<dim3(1), dim3(1024), 0, s>>>(p, segs, totals);
   }
   if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[0]), s) != hipSuccess)
     return CLE_EHIP;
+  static int occ_b1[64], occ_b2[64], occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64];
   if (ub1 > 0) {
-    const int g = persistent_grid(ub1);
-    if (dt == CLE_BF16)
-      ffn_gemm_bf16<1><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-    else
+    if (dt == CLE_BF16 && wn == 8) {
+      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8>, occ_b1, 512));
+      ffn_gemm_bf16<1, 8><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+    } else if (dt == CLE_BF16) {
+      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4>, occ_c1, 256));
+      ffn_gemm_bf16<1, 4><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+    } else {
+      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_f32<1>, occ_f1, 256));
       ffn_gemm_f32<1><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+    }
   }
   if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[1]), s) != hipSuccess)
     return CLE_EHIP;
   if (ub2 > 0) {
-    const int g = persistent_grid(ub2);
-    if (dt == CLE_BF16)
-      ffn_gemm_bf16<2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-    else
+    if (dt == CLE_BF16 && wn == 8) {
+      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8>, occ_b2, 512));
+      ffn_gemm_bf16<2, 8><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+    } else if (dt == CLE_BF16) {
+      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4>, occ_c2, 256));
+      ffn_gemm_bf16<2, 4><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+    } else {
+      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_f32<2>, occ_f2, 256));
       ffn_gemm_f32<2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+    }
   }
   if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[2]), s) != hipSuccess)
     return CLE_EHIP;
