@@ -194,25 +194,28 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 
 // Grouped GEMM tile kernel (bf16, gfx950).
 //
-// The kernel is bound by how many cache-line requests each CU keeps in
-// flight, so (a) the tile is as large as the accumulators allow, cutting the
-// re-reads of weights (once per row tile) and activations (once per column
-// tile), and (b) operands are moved with direct global->LDS loads
-// (global_load_lds_dwordx4), which need no registers, into a kStages-deep
-// ring of LDS stages, so kStages-1 K steps are in flight during each MFMA
-// step.
-//
-// Tile: kTM = 128 rows x WN wavefronts; wavefront w owns two 16-row weight
-// blocks (phase 1: the gate rows and the up rows of 16 act columns; phase 2:
-// 32 output columns) and computes all kTM rows of them.  Every direct load
-// instruction moves one 16 x 32 bf16 MFMA operand fragment (1 KiB); lane l's
-// 16 bytes land at byte 16*l of the fragment slot, which is exactly where the
-// MFMA operand read of lane l expects them, so LDS reads are contiguous and
-// conflict-free.  Row blocks past the end of a segment are skipped (no
-// loads, no MFMAs, no stores).
+// The kernel is bound by the vector-memory request path of each CU (the
+// texture address unit waits on the L1 for most cycles), so the design
+// minimises cache-line requests per useful byte:
+//  * operands move with direct global->LDS loads (global_load_lds_dwordx4,
+//    no registers) into a ring of kStages LDS stages, kStages-1 of them in
+//    flight while the MFMAs work on one;
+//  * every load instruction covers 8 rows x 128 contiguous bytes (64 K
+//    elements), i.e. 8 whole cache lines, so no line is requested twice;
+//  * lane p of a load writes LDS position 16*p of its 1 KiB slot; the lane
+//    fetches row p/8, 16-byte chunk (p%8) ^ (p/8) of the 8-row group, an XOR
+//    swizzle under which the MFMA operand reads (16 rows x one chunk per
+//    quarter-wave) hit distinct banks;
+//  * the tile is 128 rows x WN wavefronts; wavefront w owns two 16-row weight
+//    blocks (phase 1: the gate rows and the up rows of 16 act columns; phase
+//    2: 32 output columns) and computes all 128 rows of them.
+// Row blocks past the end of a segment cost no MFMAs or stores; their loads
+// repeat the segment's last row.
 constexpr int kTM = 128;
 constexpr int kMB = kTM / 16;   // 16-row blocks per tile
+constexpr int kKS = 64;         // K per stage (two MFMA K slices)
 constexpr int kStages = 3;
+constexpr int kMaxWN = 8;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gvoid;
@@ -236,27 +239,23 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-constexpr int kMaxWN = 8;
-
-// One pipeline stage: the operand fragments of one K step of a tile.
+// One pipeline stage: a 16-row x 64-K operand block is two 1 KiB slots
+// (rows 0-7, rows 8-15) of 64 lane positions.
 struct StageLDS {
-  uint4 w[kMaxWN * 4][64];  // [wave*4 + block*2 + half][lane]
-  uint4 x[kMB * 2][64];     // [rowblock*2 + half][lane]
+  uint4 w[kMaxWN * 2][2][64];  // [wave*2 + block][row group][position]
+  uint4 x[kMB][2][64];         // [row block][row group][position]
 };
-// Three stages, referenced by name (one set per kernel instantiation), so the
+// The stages, referenced by name (one set per kernel instantiation), so the
 // compiler can tell which stage each direct load writes and each read reads,
 // and waits only for the loads a read depends on.
-template <int PHASE, int WN>
-__shared__ StageLDS g_st0;
-template <int PHASE, int WN>
-__shared__ StageLDS g_st1;
-template <int PHASE, int WN>
-__shared__ StageLDS g_st2;
+template <int PHASE, int WN> __shared__ StageLDS g_st0;
+template <int PHASE, int WN> __shared__ StageLDS g_st1;
+template <int PHASE, int WN> __shared__ StageLDS g_st2;
 
 // Everything one tile needs, resolved from the segment table.
 struct TileArgs {
-  const uint16_t* w0p;  // this lane's first weight row (+ its K offset)
-  const uint16_t* w1p;  // this lane's second weight row
+  const uint16_t* w0;   // first weight row of this wavefront's block 0
+  const uint16_t* w1;   // first weight row of its block 1
   const uint16_t* A;    // first row of the tile's A operand
   uint16_t* out;        // first row of the tile's output
   int K;                // reduction length (row stride of A and W)
@@ -265,21 +264,35 @@ struct TileArgs {
   int nrows;            // valid rows of the tile (1..kTM)
 };
 
-// The K loop and epilogue of one tile with NMB active 16-row blocks (a
+// The K loop and epilogue of one tile computing NMB 16-row blocks (a
 // compile-time count, so the MFMA sequence has no data-dependent branches).
 template <int PHASE, int WN, int NMB>
 __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) {
-  constexpr int XB = kMB / WN;  // x row blocks owned by each wavefront
-  const int l16 = lane % 16, g4 = lane / 16;
-  const int KT = t.K / kBK;
-  // x fragments this wavefront loads; rows past the tile are clamped to its
-  // last row (cheap repeated reads; those output rows are never stored)
-  const uint16_t* xp[XB];
+  constexpr int XB = kMB / WN;  // x row blocks loaded by each wavefront
+  const int KT = t.K / kKS;
+  // load side: this lane fetches row lr of each 8-row group, chunk lc
+  const int lr = lane / 8, lc = (lane % 8) ^ (lane / 8);
+  const uint16_t* wp[2][2];
 #pragma unroll
-  for (int b = 0; b < XB; ++b) {
-    const int mb = wave * XB + b;
-    xp[b] = t.A + min(mb * 16 + l16, t.nrows - 1) * t.K + g4 * 8;
+  for (int g = 0; g < 2; ++g) {
+    wp[0][g] = t.w0 + (g * 8 + lr) * t.K + lc * 8;
+    wp[1][g] = t.w1 + (g * 8 + lr) * t.K + lc * 8;
   }
+  const uint16_t* xp[XB][2];
+#pragma unroll
+  for (int b = 0; b < XB; ++b)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // rows past the tile repeat its last row (never stored)
+      const int row = min((wave * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
+      xp[b][g] = t.A + row * t.K + lc * 8;
+    }
+  // read side: MFMA operand of lane `lane` for K slice h is row lane%16,
+  // chunk 4h + lane/16: row group rg, position (lane%8)*8 + (chunk ^ lane%8)
+  const int rg = (lane % 16) / 8, r8 = lane % 8;
+  const int pos0 = r8 * 8 + ((0 + lane / 16) ^ r8);
+  const int pos1 = r8 * 8 + ((4 + lane / 16) ^ r8);
+
   f32x4 acc0[NMB], acc1[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
@@ -287,45 +300,43 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
     acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // request K step KT_ into stage ST
+  // request K stage KT_ into ST
 #define CLE_ISSUE(ST, KT_)                                                          \
   {                                                                                 \
-    const int ko = (KT_) * kBK;                                                     \
-    dma16(t.w0p + ko, &ST.w[wave * 4 + 0][0]);                                      \
-    dma16(t.w0p + ko + 32, &ST.w[wave * 4 + 1][0]);                                 \
-    dma16(t.w1p + ko, &ST.w[wave * 4 + 2][0]);                                      \
-    dma16(t.w1p + ko + 32, &ST.w[wave * 4 + 3][0]);                                 \
-    _Pragma("unroll") for (int b = 0; b < XB; ++b) {                                \
-      dma16(xp[b] + ko, &ST.x[(wave * XB + b) * 2 + 0][0]);                         \
-      dma16(xp[b] + ko + 32, &ST.x[(wave * XB + b) * 2 + 1][0]);                    \
+    const int ko = (KT_) * kKS;                                                     \
+    _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                 \
+      dma16(wp[0][g] + ko, &ST.w[wave * 2 + 0][g][0]);                              \
+      dma16(wp[1][g] + ko, &ST.w[wave * 2 + 1][g][0]);                              \
     }                                                                               \
+    _Pragma("unroll") for (int b = 0; b < XB; ++b)                                  \
+      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
+        dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
   }
-  // K half outer, row block inner: every accumulator sees the two halves of
-  // a K step in the same order in every tile shape
 #define CLE_COMPUTE(ST)                                                             \
   _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                   \
-    const bf16x8 B0 = __builtin_bit_cast(bf16x8, ST.w[wave * 4 + h][lane]);         \
-    const bf16x8 B1 = __builtin_bit_cast(bf16x8, ST.w[wave * 4 + 2 + h][lane]);     \
+    const int pos = h == 0 ? pos0 : pos1;                                           \
+    const bf16x8 B0 = __builtin_bit_cast(bf16x8, ST.w[wave * 2 + 0][rg][pos]);      \
+    const bf16x8 B1 = __builtin_bit_cast(bf16x8, ST.w[wave * 2 + 1][rg][pos]);      \
     _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb) {                            \
-      const bf16x8 Af = __builtin_bit_cast(bf16x8, ST.x[mb * 2 + h][lane]);         \
+      const bf16x8 Af = __builtin_bit_cast(bf16x8, ST.x[mb][rg][pos]);              \
       acc0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B0, acc0[mb], 0, 0, 0); \
       acc1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B1, acc1[mb], 0, 0, 0); \
     }                                                                               \
   }
-  // Step KT_ (in stage CUR): wait for this wavefront's loads of step KT_ (the
-  // loads of step KT_+1 may stay in flight), barrier (every wavefront's loads
-  // of step KT_ have landed and every wavefront is done with step KT_-1),
-  // request step KT_+2 into the stage of step KT_-1, compute.  Requests are
-  // unconditional (the step index is clamped at the end, re-reading the last
-  // step into a finished stage) so that every wavefront has exactly
-  // kPerStep requests per step in flight and the compiler can track which
-  // stage each request writes.
+  // Stage KT_ (in CUR): wait for this wavefront's loads of stage KT_ (those
+  // of the next stage may stay in flight), barrier (every wavefront's loads
+  // of stage KT_ have landed and every wavefront is done with stage KT_-1),
+  // request stage KT_+2 into the buffer of stage KT_-1, compute.  Requests
+  // are unconditional (the stage index is clamped at the end, re-reading the
+  // last stage into a finished buffer) so that every wavefront always has
+  // exactly kPerStep requests per stage in flight and the compiler can tell
+  // which buffer each request writes.
   constexpr int kPerStep = 4 + 2 * XB;
-#define CLE_STEP(CUR, NXT2, KT_)                                                    \
+#define CLE_STEP(CUR, NXT, KT_)                                                     \
   {                                                                                 \
-    wait_vmcnt<kPerStep>();                                                         \
+    wait_vmcnt<kPerStep * (kStages - 2)>();                                         \
     stage_barrier();                                                                \
-    CLE_ISSUE(NXT2, min((KT_) + 2, KT - 1));                                        \
+    CLE_ISSUE(NXT, min((KT_) + kStages - 1, KT - 1));                               \
     CLE_COMPUTE(CUR);                                                               \
   }
 
@@ -350,9 +361,10 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
 #undef CLE_ISSUE
 #undef CLE_COMPUTE
 #undef CLE_STEP
-  wait_vmcnt<0>();  // the clamped tail requests have landed before stages are reused
+  wait_vmcnt<0>();  // the clamped tail requests have landed before buffers are reused
 
-  // epilogue: lane holds rows mb*16 + g4*4 + i, column l16 of each block
+  // epilogue: lane holds rows mb*16 + (lane/16)*4 + i, column lane%16 of each block
+  const int g4 = lane / 16;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
@@ -367,6 +379,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // store block by block (bounded live ranges)
   }
 }
 
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
   const int grid = gridDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  const int l16 = lane % 16, g4 = lane / 16;
+  const int l16 = lane % 16;
   const int K = PHASE == 1 ? H : I;
 
   for (int tile = logical_tile_base(grid); tile < total; tile += grid) {
@@ -393,26 +406,31 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     TileArgs t;
     t.K = K;
     t.nrows = min(kTM, sg.rows - row0);
+    // The output row stride is laundered per tile: otherwise the compiler
+    // hoists every per-row output offset (row * stride, one register per
+    // row) out of the tile loop and keeps them all live.
+    int ldo = PHASE == 1 ? I : H;
+    asm volatile("" : "+s"(ldo));
     t.A = (PHASE == 1 ? sg.a : static_cast<const uint16_t*>(sg.act)) +
           static_cast<int64_t>(row0) * K;
     const uint16_t* W = static_cast<const uint16_t*>(PHASE == 1 ? sg.w13 : sg.w2);
-    int wrow0, wrow1;
+    int wrow0, wrow1;  // first rows of this wavefront's two weight blocks
     if (PHASE == 1) {
-      wrow0 = nt * (16 * WN) + wave * 16 + l16;  // gate row
-      wrow1 = I + wrow0;                         // up row of the same act column
+      wrow0 = nt * (16 * WN) + wave * 16;  // gate rows
+      wrow1 = I + wrow0;                   // up rows of the same act columns
       t.out = static_cast<uint16_t*>(sg.act) + static_cast<int64_t>(row0) * I;
-      t.ldo = I;
       t.col = nt * (16 * WN) + wave * 16 + l16;
     } else {
-      wrow0 = nt * (32 * WN) + wave * 32 + l16;
+      wrow0 = nt * (32 * WN) + wave * 32;
       wrow1 = wrow0 + 16;
       t.out = static_cast<uint16_t*>(sg.y) + static_cast<int64_t>(row0) * H;
-      t.ldo = H;
       t.col = nt * (32 * WN) + wave * 32 + l16;
     }
-    t.w0p = W + static_cast<int64_t>(wrow0) * K + g4 * 8;
-    t.w1p = W + static_cast<int64_t>(wrow1) * K + g4 * 8;
-    switch ((t.nrows + 15) / 16) {
+    t.ldo = ldo;
+    t.w0 = W + static_cast<int64_t>(wrow0) * K;
+    t.w1 = W + static_cast<int64_t>(wrow1) * K;
+    const int nmb = (t.nrows + 15) / 16;
+    switch (nmb) {
       case 1: tile_nmb<PHASE, WN, 1>(t, wave, lane); break;
       case 2: tile_nmb<PHASE, WN, 2>(t, wave, lane); break;
       case 3: tile_nmb<PHASE, WN, 3>(t, wave, lane); break;
