@@ -50,7 +50,7 @@ class FfnDesc(ctypes.Structure):
     """Mirror of ``cle_ffn_desc``."""
     _fields_ = [("layer", _i32), ("rows", _i32), ("offsets", _vp), ("xp", _vp), ("act", _vp),
                 ("yp", _vp), ("shared_rows", _i32), ("x_shared", _vp), ("act_shared", _vp),
-                ("y_shared", _vp)]
+                ("y_shared", _vp), ("x", _vp), ("src", _vp), ("k", _i32)]
 
 
 _sig = {
@@ -120,6 +120,8 @@ def route(logits, k, topk_idx, topk_gate, stream=None):
 
 
 def dispatch(topk_idx, E, x, counts, offsets, dest, src, xp, ws, stream=None):
+    """xp may be None: the row copy is skipped (the expert launch then reads
+    the rows of x through src)."""
     T, k = topk_idx.shape
     H = x.shape[1]
     _check("cle_dispatch", _lib.cle_dispatch(
@@ -128,9 +130,11 @@ def dispatch(topk_idx, E, x, counts, offsets, dest, src, xp, ws, stream=None):
 
 
 def make_desc(layer, rows, offsets, xp, act, yp, shared_rows=0, x_shared=None, act_shared=None,
-              y_shared=None) -> FfnDesc:
+              y_shared=None, x=None, src=None, k=0) -> FfnDesc:
+    """One micro-batch of a grouped expert launch.  Pass xp=None with x, src,
+    k to read the expert-sorted rows of x in place."""
     return FfnDesc(layer, rows, _ptr(offsets), _ptr(xp), _ptr(act), _ptr(yp), shared_rows,
-                   _ptr(x_shared), _ptr(act_shared), _ptr(y_shared))
+                   _ptr(x_shared), _ptr(act_shared), _ptr(y_shared), _ptr(x), _ptr(src), k)
 
 
 def grouped_expert_ffn(descs, w13, w2, ws, w13_shared=None, w2_shared=None, events=None,

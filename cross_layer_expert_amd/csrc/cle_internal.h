@@ -49,12 +49,13 @@ struct Seg {
   void* y;              // phase-2 output rows
   const void* w13;      // [2I, H]
   const void* w2;       // [H, I]
+  const int32_t* rmap;  // NULL: A row r is a + r*H; else token rmap[r] / kdiv of a
   int32_t rows;
   int32_t t1;           // first phase-1 tile of this segment
   int32_t t2;           // first phase-2 tile of this segment
-  int32_t pad_;
+  int32_t kdiv;
 };
-static_assert(sizeof(Seg) == 56, "Seg layout");
+static_assert(sizeof(Seg) == 64, "Seg layout");
 
 constexpr size_t kFfnHeader = 256;  // totals live in the first 256 bytes
 

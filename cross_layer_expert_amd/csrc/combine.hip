@@ -49,7 +49,11 @@ struct Vec<float> {
   }
 };
 
-template <typename T>
+// KMAX > 0: k <= KMAX slots, whose destinations and gates are held in
+// registers so that all slot rows of a column chunk are requested before the
+// first one is used.  KMAX == 0: any k, one slot at a time.  Both sum the
+// slots in order 0..k-1.
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp,
                                                       const int* __restrict__ dest,
                                                       const float* __restrict__ gate, int T_,
@@ -62,18 +66,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp,
   if (t >= T_) return;
   const int* drow = dest + static_cast<int64_t>(t) * k;
   const float* grow = gate + static_cast<int64_t>(t) * k;
+  int d[KMAX > 0 ? KMAX : 1];
+  float g[KMAX > 0 ? KMAX : 1];
+  if (KMAX > 0) {
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      d[s] = s < k ? drow[s] : -1;
+      g[s] = s < k ? grow[s] : 0.0f;
+    }
+  }
   for (int c = lane * N; c < H; c += kWave * N) {
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-    for (int s = 0; s < k; ++s) {
-      const int d = drow[s];
-      if (d < 0) continue;
-      const float g = grow[s];
-      float v[N];
-      Vec<T>::load(yp + static_cast<int64_t>(d) * H + c, v);
+    if (KMAX > 0) {
+      float v[KMAX > 0 ? KMAX : 1][N];
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      for (int s = 0; s < KMAX; ++s)
+        if (d[s] >= 0) Vec<T>::load(yp + static_cast<int64_t>(d[s]) * H + c, v[s]);
+#pragma unroll
+      for (int s = 0; s < KMAX; ++s)
+        if (d[s] >= 0) {
+#pragma unroll
+          for (int i = 0; i < N; ++i) acc[i] = fmaf(g[s], v[s][i], acc[i]);
+        }
+    } else {
+      for (int s = 0; s < k; ++s) {
+        const int ds = drow[s];
+        if (ds < 0) continue;
+        const float gs = grow[s];
+        float v[N];
+        Vec<T>::load(yp + static_cast<int64_t>(ds) * H + c, v);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] = fmaf(gs, v[i], acc[i]);
+      }
     }
     for (int q = 0; q < n_shared; ++q) {
       float v[N];
@@ -89,6 +115,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp,
     }
     Vec<T>::store(y + static_cast<int64_t>(t) * H + c, acc);
   }
+}
+
+template <typename T>
+void launch_combine(dim3 grid, hipStream_t s, const T* yp, const int* dest, const float* gate,
+                    int T_, int k, int H, const T* ysh, int ns, const T* res, T* y) {
+  if (k <= 8)
+    combine_kernel<T, 8><<<grid, dim3(256), 0, s>>>(yp, dest, gate, T_, k, H, ysh, ns, res, y);
+  else
+    combine_kernel<T, 0><<<grid, dim3(256), 0, s>>>(yp, dest, gate, T_, k, H, ysh, ns, res, y);
 }
 
 }  // namespace
@@ -107,17 +142,15 @@ extern "C" cle_status cle_combine(const void* yp, const int32_t* dest, const flo
   if (!aligned(yp, 16) || !aligned(y, 16) || (y_shared && !aligned(y_shared, 16)) ||
       (residual && !aligned(residual, 16)))
     return CLE_EINVAL;
-  const dim3 grid((T + 3) / 4), block(256);
+  const dim3 grid((T + 3) / 4);
   hipStream_t s = as_stream(stream);
   if (dt == CLE_BF16)
-    combine_kernel<uint16_t><<<grid, block, 0, s>>>(
-        static_cast<const uint16_t*>(yp), dest, topk_gate, T, k, H,
-        static_cast<const uint16_t*>(y_shared), n_shared, static_cast<const uint16_t*>(residual),
-        static_cast<uint16_t*>(y));
+    launch_combine<uint16_t>(grid, s, static_cast<const uint16_t*>(yp), dest, topk_gate, T, k, H,
+                             static_cast<const uint16_t*>(y_shared), n_shared,
+                             static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y));
   else
-    combine_kernel<float><<<grid, block, 0, s>>>(
-        static_cast<const float*>(yp), dest, topk_gate, T, k, H,
-        static_cast<const float*>(y_shared), n_shared, static_cast<const float*>(residual),
-        static_cast<float*>(y));
+    launch_combine<float>(grid, s, static_cast<const float*>(yp), dest, topk_gate, T, k, H,
+                          static_cast<const float*>(y_shared), n_shared,
+                          static_cast<const float*>(residual), static_cast<float*>(y));
   return launch_status();
 }

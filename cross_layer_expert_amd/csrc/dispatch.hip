@@ -43,8 +43,9 @@ __global__ __launch_bounds__(256) void dispatch_count(const int* __restrict__ id
 // Turns chunk counts into absolute chunk bases in place and writes counts
 // and offsets.
 __global__ __launch_bounds__(1024) void dispatch_scan(int* __restrict__ chunk_hist, int64_t chunks,
-                                                      int E, int* __restrict__ counts,
-                                                      int* __restrict__ offsets) {
+                                                      int E, int64_t A, int* __restrict__ counts,
+                                                      int* __restrict__ offsets,
+                                                      int* __restrict__ src) {
   __shared__ int tot[CLE_MAX_E];
   __shared__ int part[1024];
   const int tid = threadIdx.x;
@@ -75,6 +76,8 @@ __global__ __launch_bounds__(1024) void dispatch_scan(int* __restrict__ chunk_hi
     offsets[tid] = excl;
   }
   if (tid == E - 1) offsets[E] = part[tid];
+  // positions past the valid assignments (dropped ids) have no source
+  for (int64_t p = part[E - 1] + tid; p < A; p += blockDim.x) src[p] = -1;
   __syncthreads();
   if (tid < E) tot[tid] = excl;
   __syncthreads();
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter(const int* __restrict__ 
 template <typename T>
 __global__ __launch_bounds__(256) void dispatch_gather(const T* __restrict__ x, int64_t A, int k,
                                                        int H, const int* __restrict__ offsets,
-                                                       int E, int* __restrict__ src,
+                                                       int E, const int* __restrict__ src,
                                                        T* __restrict__ xp) {
   constexpr int VEC = 16 / sizeof(T);
   const int wave = threadIdx.x / kWave;
@@ -169,7 +172,6 @@ __global__ __launch_bounds__(256) void dispatch_gather(const T* __restrict__ x, 
     const uint4* in = reinterpret_cast<const uint4*>(x + t * H);
     for (int c = lane; c < nvec; c += kWave) out[c] = in[c];
   } else {
-    if (lane == 0) src[p] = -1;
     for (int c = lane; c < nvec; c += kWave) out[c] = make_uint4(0, 0, 0, 0);
   }
 }
@@ -187,7 +189,8 @@ extern "C" cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k
   if (!counts || !offsets) return CLE_EINVAL;
   const int64_t A = static_cast<int64_t>(T) * k;
   if (A > INT32_MAX) return CLE_EUNSUPPORTED;
-  if (A > 0 && (!topk_idx || !x || !dest || !src || !xp)) return CLE_EINVAL;
+  if (A > 0 && (!topk_idx || !dest || !src)) return CLE_EINVAL;
+  if (A > 0 && xp && !x) return CLE_EINVAL;
   if (!aligned(x, 16) || !aligned(xp, 16)) return CLE_EINVAL;
   const size_t need = cle_workspace_bytes(CLE_OP_DISPATCH, T, E, k, 0, 1);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return CLE_EWORKSPACE;
@@ -197,12 +200,13 @@ extern "C" cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k
   if (chunks > 0) {
     dispatch_count<<<dim3(static_cast<unsigned>(chunks)), dim3(256), 0, s>>>(topk_idx, A, E, hist);
   }
-  dispatch_scan<<<dim3(1), dim3(1024), 0, s>>>(hist, chunks, E, counts, offsets);
+  dispatch_scan<<<dim3(1), dim3(1024), 0, s>>>(hist, chunks, E, A, counts, offsets, src);
   if (A == 0) return launch_status();
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
   dispatch_scatter<<<dim3(static_cast<unsigned>(chunks)), dim3(256), 0, s>>>(
       topk_idx, A, E, id_bits, hist, dest, src);
+  if (!xp) return launch_status();
   const dim3 ggrid(static_cast<unsigned>((A + 3) / 4));
   if (dt == CLE_BF16)
     dispatch_gather<uint16_t><<<ggrid, dim3(256), 0, s>>>(

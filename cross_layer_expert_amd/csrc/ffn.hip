@@ -45,6 +45,9 @@ struct DescDev {
   const void* x_shared;
   void* act_shared;
   void* y_shared;
+  const void* x;      // token rows, read through src when xp is NULL
+  const int* src;
+  int k;
 };
 
 struct PlanArgs {
@@ -57,6 +60,7 @@ struct PlanArgs {
   int E, ns, H, I, esz;
   int tm, tn1, tn2;  // tile rows, phase-1 act columns, phase-2 output columns
 };
+static_assert(sizeof(PlanArgs) <= 4096, "kernel argument size");
 
 // ---------------------------------------------------------------- planning
 // Row range [lo, hi) of routed expert e, clamped to the descriptor's rows so
@@ -117,7 +121,15 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
       seg_range(d, e, lo, hi);
       const int64_t off = lo;
       g.rows = hi - lo;
-      g.a = reinterpret_cast<const uint16_t*>(static_cast<const char*>(d.xp) + off * H * esz);
+      if (d.xp) {
+        g.a = reinterpret_cast<const uint16_t*>(static_cast<const char*>(d.xp) + off * H * esz);
+        g.rmap = nullptr;
+        g.kdiv = 1;
+      } else {
+        g.a = static_cast<const uint16_t*>(d.x);
+        g.rmap = d.src + off;
+        g.kdiv = d.k;
+      }
       g.act = static_cast<char*>(d.act) + off * I * esz;
       g.y = static_cast<char*>(d.yp) + off * H * esz;
       const int64_t we = static_cast<int64_t>(d.layer) * p.E + e;
@@ -127,6 +139,8 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
       const int64_t q = e - p.E, R = d.shared_rows;
       g.rows = d.shared_rows;
       g.a = reinterpret_cast<const uint16_t*>(d.x_shared);
+      g.rmap = nullptr;
+      g.kdiv = 1;
       g.act = static_cast<char*>(d.act_shared) + q * R * I * esz;
       g.y = static_cast<char*>(d.y_shared) + q * R * H * esz;
       const int64_t we = static_cast<int64_t>(d.layer) * p.ns + q;
@@ -135,7 +149,6 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
     }
     g.t1 = t1;
     g.t2 = t2;
-    g.pad_ = 0;
     segs[p.seg_base + s] = g;
     const int mt = (g.rows + p.tm - 1) / p.tm;
     t1 += mt * n1;
@@ -256,7 +269,10 @@ template <int PHASE, int WN> __shared__ StageLDS g_st2;
 struct TileArgs {
   const uint16_t* w0;   // first weight row of this wavefront's block 0
   const uint16_t* w1;   // first weight row of its block 1
-  const uint16_t* A;    // first row of the tile's A operand
+  const uint16_t* A;    // first row of the tile's A operand (rmap == NULL), or the
+                        // token rows the row map points into
+  const int* rmap;      // NULL, or the row map from this tile's first row
+  int kdiv;             // row r of the tile is token rmap[r] / kdiv of A
   uint16_t* out;        // first row of the tile's output
   int K;                // reduction length (row stride of A and W)
   int ldo;              // output row stride
@@ -285,7 +301,8 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
     for (int g = 0; g < 2; ++g) {
       // rows past the tile repeat its last row (never stored)
       const int row = min((wave * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
-      xp[b][g] = t.A + row * t.K + lc * 8;
+      const int64_t arow = t.rmap ? static_cast<int64_t>(t.rmap[row] / t.kdiv) : row;
+      xp[b][g] = t.A + arow * t.K + lc * 8;
     }
   // read side: MFMA operand of lane `lane` for K slice h is row lane%16,
   // chunk 4h + lane/16: row group rg, position (lane%8)*8 + (chunk ^ lane%8)
@@ -411,8 +428,16 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     // row) out of the tile loop and keeps them all live.
     int ldo = PHASE == 1 ? I : H;
     asm volatile("" : "+s"(ldo));
-    t.A = (PHASE == 1 ? sg.a : static_cast<const uint16_t*>(sg.act)) +
-          static_cast<int64_t>(row0) * K;
+    if (PHASE == 1 && sg.rmap) {
+      t.A = sg.a;
+      t.rmap = sg.rmap + row0;
+      t.kdiv = sg.kdiv;
+    } else {
+      t.A = (PHASE == 1 ? sg.a : static_cast<const uint16_t*>(sg.act)) +
+            static_cast<int64_t>(row0) * K;
+      t.rmap = nullptr;
+      t.kdiv = 1;
+    }
     const uint16_t* W = static_cast<const uint16_t*>(PHASE == 1 ? sg.w13 : sg.w2);
     int wrow0, wrow1;  // first rows of this wavefront's two weight blocks
     if (PHASE == 1) {
@@ -465,7 +490,11 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const Seg* __restrict__ segs
       const int row = mi * kBM + e / 64;
       const int col = nt * 64 + e % 64;
       if (row >= sg.rows) continue;
-      const float* a = A + static_cast<int64_t>(row) * K;
+      const float* a =
+          (PHASE == 1 && sg.rmap)
+              ? static_cast<const float*>(static_cast<const void*>(sg.a)) +
+                    static_cast<int64_t>(sg.rmap[row] / sg.kdiv) * K
+              : A + static_cast<int64_t>(row) * K;
       if (PHASE == 1) {
         const float* wg = W + static_cast<int64_t>(col) * K;
         const float* wu = W + static_cast<int64_t>(I + col) * K;
@@ -534,8 +563,10 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
   for (int j = 0; j < n_desc; ++j) {
     const cle_ffn_desc& q = d[j];
     if (q.layer < 0 || q.layer >= L || q.rows < 0 || !q.offsets) return CLE_EINVAL;
-    if (q.rows > 0 && (!q.xp || !q.act || !q.yp)) return CLE_EINVAL;
-    if (!aligned(q.xp, 16) || !aligned(q.act, 16) || !aligned(q.yp, 16)) return CLE_EINVAL;
+    if (q.rows > 0 && (!q.act || !q.yp)) return CLE_EINVAL;
+    if (q.rows > 0 && !q.xp && (!q.x || !q.src || q.k < 1)) return CLE_EINVAL;
+    if (!aligned(q.xp, 16) || !aligned(q.x, 16) || !aligned(q.act, 16) || !aligned(q.yp, 16))
+      return CLE_EINVAL;
     if (n_shared > 0) {
       if (q.shared_rows < 0) return CLE_EINVAL;
       if (q.shared_rows > 0 && (!q.x_shared || !q.act_shared || !q.y_shared)) return CLE_EINVAL;
@@ -563,7 +594,8 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
     for (int j = 0; j < p.nd; ++j) {
       const cle_ffn_desc& q = d[c + j];
       p.d[j] = DescDev{q.layer, q.rows, q.offsets, q.xp, q.act, q.yp,
-                       n_shared > 0 ? q.shared_rows : 0, q.x_shared, q.act_shared, q.y_shared};
+                       n_shared > 0 ? q.shared_rows : 0, q.x_shared, q.act_shared, q.y_shared,
+                       q.x, q.src, q.k};
     }
     p.w13 = w13;
     p.w2 = w2;

@@ -30,7 +30,8 @@ class Engine:
     logits: tensor [n, L, T, E] float32 on the device, h0: tensor [n, T, H].
     """
 
-    def __init__(self, weights, logits, h0, D, k, policy, m, start_layers=None, stream=None):
+    def __init__(self, weights, logits, h0, D, k, policy, m, start_layers=None, stream=None,
+                 fused_gather=True):
         self.w13, self.w2, self.w13s, self.w2s = weights
         self.L, self.E, I2, self.H = self.w13.shape
         self.I = I2 // 2
@@ -51,7 +52,10 @@ class Engine:
         self.offsets = torch.zeros((n, E + 1), **i32)
         self.dest = torch.empty((n, A), **i32)
         self.src = torch.empty((n, A), **i32)
-        self.xp = torch.empty((n, A, H), dtype=dt, device=dev)
+        # fused_gather: the expert launch reads token rows through src, so the
+        # expert-sorted copy xp is never materialised
+        self.fused = fused_gather
+        self.xp = None if fused_gather else torch.empty((n, A, H), dtype=dt, device=dev)
         self.act = torch.empty((n, A, I), dtype=dt, device=dev)
         self.yp = torch.empty((n, A, H), dtype=dt, device=dev)
         if self.ns:
@@ -71,7 +75,12 @@ class Engine:
         self.reset()
 
     def _desc(self, j):
-        d = make_desc(0, self.T * self.k, self.offsets[j], self.xp[j], self.act[j], self.yp[j])
+        if self.fused:
+            d = make_desc(0, self.T * self.k, self.offsets[j], None, self.act[j], self.yp[j],
+                          x=self.h[j], src=self.src[j], k=self.k)
+        else:
+            d = make_desc(0, self.T * self.k, self.offsets[j], self.xp[j], self.act[j],
+                          self.yp[j])
         if self.ns:
             d.shared_rows = self.T
             d.x_shared = self.h[j].data_ptr()
@@ -98,7 +107,7 @@ class Engine:
         s = self.stream
         route(self.logits[j, self.l[j]], self.k, self.idx[j], self.gates[j], stream=s)
         dispatch(self.idx[j], self.E, self.h[j], self.counts[j], self.offsets[j], self.dest[j],
-                 self.src[j], self.xp[j], self.ws_dispatch, stream=s)
+                 self.src[j], None if self.fused else self.xp[j], self.ws_dispatch, stream=s)
 
     def schedule(self) -> list:
         """Workloads to the host, then Schedule(S, m) in the host library."""

@@ -93,10 +93,13 @@ cle_status cle_route(const float* logits, int32_t T, int32_t E, int32_t k,
  *   offsets  [E+1] int32 out: exclusive prefix sum of counts.
  *   dest     [T*k] int32 out: dest[a] = offsets[e] + #{a' < a : idx[a'] = e}.
  *   src      [T*k] int32 out: inverse permutation, src[dest[a]] = a.
- *   xp       [T*k, H] (dt) out: xp[p] = x[src[p] / k].
+ *   xp       [T*k, H] (dt) out: xp[p] = x[src[p] / k]; may be NULL, then the row
+ *            copy is skipped (cle_grouped_expert_ffn can read the rows of x
+ *            through src instead, see cle_ffn_desc).
  *   ws       workspace of at least cle_workspace_bytes(CLE_OP_DISPATCH, T, E, k, ...).
  * An expert id outside [0, E) is dropped: it is counted nowhere, its dest is
- * -1, and the trailing rows p >= offsets[E] get src = -1 and zero xp rows.
+ * -1, and the trailing positions p >= offsets[E] get src = -1 (and zero xp
+ * rows).
  * Requires H % 8 == 0, 1 <= k, 1 <= E <= CLE_MAX_E.
  */
 cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
@@ -113,13 +116,18 @@ typedef struct {
   int32_t layer;            /* in [0, L) */
   int32_t rows;             /* rows of xp / act / yp (= T*k of the micro-batch) */
   const int32_t* offsets;   /* [E+1] from cle_dispatch */
-  const void* xp;           /* [rows, H] (dt) */
+  const void* xp;           /* [rows, H] (dt) expert-sorted rows, or NULL (see x) */
   void* act;                /* [rows, I] (dt) out: silu(G) * U */
   void* yp;                 /* [rows, H] (dt) out: expert outputs, one per assignment */
   int32_t shared_rows;      /* rows of x_shared (0 when n_shared == 0) */
   const void* x_shared;     /* [shared_rows, H] (dt), rows for the shared experts */
   void* act_shared;         /* [n_shared, shared_rows, I] (dt) out */
   void* y_shared;           /* [n_shared, shared_rows, H] (dt) out */
+  /* Used when xp is NULL: expert-sorted row p is x[src[p] / k], read in place
+   * (the dispatch row copy fused into the expert launch; same results). */
+  const void* x;            /* [rows / k, H] (dt) token rows */
+  const int32_t* src;       /* [rows] from cle_dispatch */
+  int32_t k;                /* experts per token */
 } cle_ffn_desc;
 
 /*

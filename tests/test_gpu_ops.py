@@ -192,7 +192,8 @@ def test_workload_stats_worked_example():
 @pytest.mark.parametrize("T,k,E,H,ns,dtype,res", [
     (16, 2, 8, 64, 0, "f32", True), (2048, 8, 128, 2048, 0, "bf16", True),
     (1024, 6, 64, 2048, 2, "bf16", True), (37, 3, 5, 72, 1, "bf16", False),
-    (5, 1, 1, 8, 0, "f32", False)])
+    (5, 1, 1, 8, 0, "f32", False), (9, 12, 16, 64, 1, "bf16", True),
+    (6, 9, 9, 16, 0, "f32", True)])
 def test_combine(T, k, E, H, ns, dtype, res):
     dev = device()
     rng = np.random.default_rng(T + H)
@@ -339,3 +340,49 @@ def test_ffn_rows_independent_of_launch_mates(dtype):
     _run_ffn(case, which=[2, 0])
     assert np.array_equal(bits_of(case["keep"][0]["yp"]), joint[0])
     assert np.array_equal(bits_of(case["keep"][2]["yp"]), joint[2])
+
+
+@pytest.mark.parametrize("dtype,k", [("bf16", 1), ("bf16", 3), ("f32", 2)])
+def test_ffn_reads_rows_through_src(dtype, k):
+    """Rows read in place through the dispatch permutation (xp = NULL) give the
+    same bits as rows read from a materialised xp, and match the oracle."""
+    dev = device()
+    H, I, E, L = (256, 128, 8, 2) if dtype == "bf16" else (64, 128, 8, 2)
+    rng = np.random.default_rng(21 + k)
+    sizes = [5, 0, 70, 1, 200, 16, 33, 0]
+    rows = sum(sizes)
+    ntok = -(-rows // k)
+    x = synth.store(rng.standard_normal((ntok, H)).astype(np.float32), dtype)
+    src = rng.permutation(ntok * k)[:rows].astype(np.int32)   # any assignment ids
+    xp = x[src // k]
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    cfg = synth.Config("case", L=L, H=H, E=E, k=1, I=I, D=1, n=1, T=1, dtype=dtype)
+    w13, w2, _, _ = synth.weights_numpy(cfg, 3)
+    W13, W2 = to_dev(w13, dtype, dev), to_dev(w2, dtype, dev)
+    t_off = torch.from_numpy(offsets).to(dev)
+    outs = []
+    for fused in (False, True):
+        act = torch.zeros((rows, I), dtype=W13.dtype, device=dev)
+        yp = torch.zeros((rows, H), dtype=W13.dtype, device=dev)
+        if fused:
+            # the descriptor holds raw addresses: keep its tensors alive
+            xt, st = to_dev(x, dtype, dev), torch.from_numpy(src).to(dev)
+            d = cle.make_desc(1, rows, t_off, None, act, yp, x=xt, src=st, k=k)
+            keep = (xt, st)
+        else:
+            xpt = to_dev(xp, dtype, dev)
+            d = cle.make_desc(1, rows, t_off, xpt, act, yp)
+            keep = (xpt, )
+        ws = torch.empty(cle.workspace_bytes(cle.OP_FFN, 0, E, 1, 0, 1) // 4, dtype=torch.int32,
+                         device=dev)
+        cle.grouped_expert_ffn([d], W13, W2, ws)
+        torch.cuda.synchronize()
+        outs.append(bits_of(yp))
+        del keep
+    assert np.array_equal(outs[0], outs[1])
+    ref = oracle.expert_ffn(oracle.widen(xp, dtype), offsets, oracle.widen(w13[1], dtype),
+                            oracle.widen(w2[1], dtype))
+    got = oracle.widen(outs[1].view(np.uint16) if dtype == "bf16" else outs[1].view(np.float32),
+                       dtype)
+    tol = (BF16_MAX_ABS, BF16_REL) if dtype == "bf16" else (F32_TOL, F32_TOL)
+    check_close(got, ref, *tol, what=f"fused {dtype} k={k}")
