@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +34,30 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "expert tokens/s per cross-layer MoE step; % bf16 MFMA peak; under-util 1-u"
+PROFILE = os.path.join(ROOT, "profiles", "ffn_gemm_gate_up_qwen3.md")
+KERNEL_SOURCES = ("cross_layer_expert_amd/csrc/ffn.hip", "cross_layer_expert_amd/csrc/cle_internal.h")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed rocprofv3 FETCH_SIZE +
+    WRITE_SIZE summary, or None when that summary is for another workload or
+    the kernel sources changed since the counters were taken."""
+    try:
+        text = open(PROFILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and not line.startswith((" ", "|", "#")):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.split()[0] if val.split() else ""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("workload") != workload or fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 class HipEvents:
@@ -269,11 +294,13 @@ def main():
     if ai1 < ridge:
         ach = B1 / K / (t1 / K) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(ach / HBM_PEAK_GBS, 4))
     else:
         ach = F1 / K / (t1 / K) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None)
+                    frac=round(ach / BF16_PEAK_TFLOPS, 4))
+    default_run = args.policy == "cumutil" and args.m is None and args.seed == 0
+    roof["traffic"] = measured_traffic(cfg.name) if default_run else None
     roof.update(kernel="ffn_gemm_bf16<1> (grouped gate/up + SwiGLU)",
                 mean_launch_us=round(t1 / K * 1e6, 2),
                 algorithmic_bytes_per_launch=int(B1 / K), flops_per_launch=int(F1 / K))
