@@ -4,7 +4,8 @@ Argument marshalling only: every step of the path runs in the library's HIP
 kernels (or, for ``schedule_step``, its host C++).  Tensors are torch tensors
 on the GPU; PyTorch provides device memory and streams.  If ``libcle.so`` is
 missing or fails to load, importing this package raises -- there is no
-fallback implementation.
+fallback implementation.  ``CLE_LIBRARY`` names another build of the same
+library to load instead (for comparing builds); it must exist too.
 """
 from __future__ import annotations
 
@@ -14,7 +15,7 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcle.so")
+LIB_PATH = os.environ.get("CLE_LIBRARY") or os.path.join(_PKG, "libcle.so")
 
 OK, EINVAL, EHIP, EWORKSPACE, EUNSUPPORTED = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1

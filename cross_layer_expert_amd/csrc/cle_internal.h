@@ -53,7 +53,9 @@ struct Seg {
   int32_t rows;
   int32_t t1;           // first phase-1 tile of this segment
   int32_t t2;           // first phase-2 tile of this segment
-  int32_t kdiv;
+  int16_t kdiv;
+  uint16_t kkey;        // K-order key of the segment's weights (a function of
+                        // layer and expert only)
 };
 static_assert(sizeof(Seg) == 64, "Seg layout");
 

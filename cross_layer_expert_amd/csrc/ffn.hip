@@ -14,9 +14,13 @@
 //            64 rows x 64 act columns, K = H; gate and up rows of the same
 //            act columns in one tile, so the SwiGLU epilogue is local.
 //   phase 2  same scheduler: 64 rows x 128 output columns, K = I.
-// bf16 path: v_mfma_f32_16x16x32_bf16 (gfx950), fp32 accumulation, one fixed
-// K order for every tile, no split-K, so a row's result does not depend on
-// which other segments share the launch.  A (activation) tiles are staged in
+// bf16 path: v_mfma_f32_16x16x32_bf16 (gfx950), fp32 accumulation, no
+// split-K.  The K loop over one weight block starts at a stage picked by the
+// block's (layer, expert) alone and wraps around, so a row's result does not
+// depend on which other segments share the launch, while tiles of different
+// experts read different K offsets at the same time (tiles that all started
+// at K = 0 would read addresses with equal low bits from thousands of rows at
+// once and crowd the same HBM channels).  A (activation) tiles are staged in
 // LDS and shared by the four wavefronts; each wavefront streams its own
 // weight rows straight into registers in the MFMA operand layout.
 // Consecutive logical tiles go to one XCD (workgroups are dealt round-robin
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
       } else {
         g.a = static_cast<const uint16_t*>(d.x);
         g.rmap = d.src + off;
-        g.kdiv = d.k;
+        g.kdiv = static_cast<int16_t>(d.k);
       }
       g.act = static_cast<char*>(d.act) + off * I * esz;
       g.y = static_cast<char*>(d.yp) + off * H * esz;
@@ -147,6 +151,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
       g.w13 = static_cast<const char*>(p.w13s) + we * 2 * I * H * esz;
       g.w2 = static_cast<const char*>(p.w2s) + we * H * I * esz;
     }
+    g.kkey = static_cast<uint16_t>(d.layer * 7 + e * 5);  // e counts shared experts after E
     g.t1 = t1;
     g.t2 = t2;
     segs[p.seg_base + s] = g;
@@ -275,6 +280,7 @@ struct TileArgs {
   int kdiv;             // row r of the tile is token rmap[r] / kdiv of A
   uint16_t* out;        // first row of the tile's output
   int K;                // reduction length (row stride of A and W)
+  int rot;              // first K stage of the loop (it wraps around at K)
   int ldo;              // output row stride
   int col;              // this lane's first output column
   int nrows;            // valid rows of the tile (1..kTM)
@@ -320,7 +326,9 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   // request K stage KT_ into ST
 #define CLE_ISSUE(ST, KT_)                                                          \
   {                                                                                 \
-    const int ko = (KT_) * kKS;                                                     \
+    int kr = (KT_) + t.rot;                                                         \
+    kr -= kr >= KT ? KT : 0;                                                        \
+    const int ko = kr * kKS;                                                        \
     _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                 \
       dma16(wp[0][g] + ko, &ST.w[wave * 2 + 0][g][0]);                              \
       dma16(wp[1][g] + ko, &ST.w[wave * 2 + 1][g][0]);                              \
@@ -422,6 +430,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     const int row0 = mi * kTM;
     TileArgs t;
     t.K = K;
+    t.rot = sg.kkey % (K / kKS);
     t.nrows = min(kTM, sg.rows - row0);
     // The output row stride is laundered per tile: otherwise the compiler
     // hoists every per-row output offset (row * stride, one register per
