@@ -10,19 +10,18 @@
 //            segment per (micro-batch, routed expert) and per shared expert)
 //            in the workspace, with an exclusive prefix of the tile counts of
 //            both phases; totals go to the workspace header.
-//   phase 1  persistent kernel over all (segment, n-tile, m-tile) tiles:
-//            64 rows x 64 act columns, K = H; gate and up rows of the same
-//            act columns in one tile, so the SwiGLU epilogue is local.
-//   phase 2  same scheduler: 64 rows x 128 output columns, K = I.
+//   phase 1  persistent kernel over all (segment, n-tile, m-tile) tiles,
+//            K = H.  bf16: 128 rows x 128 act columns (the gate and up rows
+//            of the same act columns are in one tile, so the SwiGLU epilogue
+//            is local); f32: 64 x 64.
+//   phase 2  same scheduler, K = I.  bf16: 128 rows x 256 output columns.
 // bf16 path: v_mfma_f32_16x16x32_bf16 (gfx950), fp32 accumulation, no
 // split-K.  The K loop over one weight block starts at a stage picked by the
 // block's (layer, expert) alone and wraps around, so a row's result does not
 // depend on which other segments share the launch, while tiles of different
 // experts read different K offsets at the same time (tiles that all started
 // at K = 0 would read addresses with equal low bits from thousands of rows at
-// once and crowd the same HBM channels).  A (activation) tiles are staged in
-// LDS and shared by the four wavefronts; each wavefront streams its own
-// weight rows straight into registers in the MFMA operand layout.
+// once and crowd the same HBM channels).
 // Consecutive logical tiles go to one XCD (workgroups are dealt round-robin
 // over the 8 XCDs) so tiles reading the same weight rows share that XCD's L2.
 #include "cle_internal.h"
@@ -212,28 +211,33 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 
 // Grouped GEMM tile kernel (bf16, gfx950).
 //
-// The kernel is bound by the vector-memory request path of each CU (the
-// texture address unit waits on the L1 for most cycles), so the design
-// minimises cache-line requests per useful byte:
-//  * operands move with direct global->LDS loads (global_load_lds_dwordx4,
-//    no registers) into a ring of kStages LDS stages, kStages-1 of them in
-//    flight while the MFMAs work on one;
-//  * every load instruction covers 8 rows x 128 contiguous bytes (64 K
-//    elements), i.e. 8 whole cache lines, so no line is requested twice;
-//  * lane p of a load writes LDS position 16*p of its 1 KiB slot; the lane
-//    fetches row p/8, 16-byte chunk (p%8) ^ (p/8) of the 8-row group, an XOR
-//    swizzle under which the MFMA operand reads (16 rows x one chunk per
-//    quarter-wave) hit distinct banks;
-//  * the tile is 128 rows x WN wavefronts; wavefront w owns two 16-row weight
-//    blocks (phase 1: the gate rows and the up rows of 16 act columns; phase
-//    2: 32 output columns) and computes all 128 rows of them.
+// A tile is 128 rows x (WN * NB) weight blocks of 16 rows.  Wavefront w owns
+// NB consecutive weight blocks -- phase 1: NB/2 blocks of gate rows and the
+// NB/2 blocks of up rows of the same act columns, so the SwiGLU epilogue is
+// local; phase 2: NB blocks of output columns -- and computes all 128 rows of
+// them.  The standard tile is WN = 8 wavefronts x NB = 2 blocks (128 act
+// columns / 256 output columns); shapes that do not divide into it use
+// WN = 4 x NB = 2.  (Four wavefronts x four blocks reads 40 % fewer operand
+// bytes from LDS per stage but measured slower: with one wavefront per SIMD
+// the memory and barrier stalls of a stage are not hidden.)
+//
+//  * Operands move with direct global->LDS loads (global_load_lds_dwordx4, no
+//    registers) into a ring of kStages LDS stages, two stages in flight.
+//  * Every load instruction covers 8 rows x 128 contiguous bytes (64 K
+//    elements), i.e. 8 whole cache lines: the vector memory path takes 16
+//    bytes per lane at full rate only when each quad of lanes reads 64
+//    contiguous bytes, which the 16-rows-per-instruction MFMA operand layout
+//    does not, so the operands are re-laid out through LDS.  Lane p writes
+//    LDS position 16*p of its 1 KiB slot and fetches row p/8, 16-byte chunk
+//    (p%8) ^ (p/8) of the 8-row group: an XOR swizzle under which the operand
+//    reads (16 rows x one chunk per quarter-wave) hit distinct banks.
 // Row blocks past the end of a segment cost no MFMAs or stores; their loads
 // repeat the segment's last row.
 constexpr int kTM = 128;
 constexpr int kMB = kTM / 16;   // 16-row blocks per tile
 constexpr int kKS = 64;         // K per stage (two MFMA K slices)
 constexpr int kStages = 3;
-constexpr int kMaxWN = 8;
+constexpr int kBlocks = 16;     // most weight blocks per tile (WN * NB)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gvoid;
@@ -260,20 +264,20 @@ __device__ __forceinline__ void stage_barrier() {
 // One pipeline stage: a 16-row x 64-K operand block is two 1 KiB slots
 // (rows 0-7, rows 8-15) of 64 lane positions.
 struct StageLDS {
-  uint4 w[kMaxWN * 2][2][64];  // [wave*2 + block][row group][position]
-  uint4 x[kMB][2][64];         // [row block][row group][position]
+  uint4 w[kBlocks][2][64];  // [wave * NB + block][row group][position]
+  uint4 x[kMB][2][64];      // [row block][row group][position]
 };
 // The stages, referenced by name (one set per kernel instantiation), so the
 // compiler can tell which stage each direct load writes and each read reads,
 // and waits only for the loads a read depends on.
-template <int PHASE, int WN> __shared__ StageLDS g_st0;
-template <int PHASE, int WN> __shared__ StageLDS g_st1;
-template <int PHASE, int WN> __shared__ StageLDS g_st2;
+template <int PHASE, int WN, int NB> __shared__ StageLDS g_st0;
+template <int PHASE, int WN, int NB> __shared__ StageLDS g_st1;
+template <int PHASE, int WN, int NB> __shared__ StageLDS g_st2;
 
 // Everything one tile needs, resolved from the segment table.
 struct TileArgs {
-  const uint16_t* w0;   // first weight row of this wavefront's block 0
-  const uint16_t* w1;   // first weight row of its block 1
+  const uint16_t* wlo;  // first weight row of this wavefront's blocks 0 .. NB/2-1
+  const uint16_t* whi;  // first weight row of its blocks NB/2 .. NB-1
   const uint16_t* A;    // first row of the tile's A operand (rmap == NULL), or the
                         // token rows the row map points into
   const int* rmap;      // NULL, or the row map from this tile's first row
@@ -282,24 +286,45 @@ struct TileArgs {
   int K;                // reduction length (row stride of A and W)
   int rot;              // first K stage of the loop (it wraps around at K)
   int ldo;              // output row stride
-  int col;              // this lane's first output column
+  int col;              // this lane's output column in the wavefront's first block
   int nrows;            // valid rows of the tile (1..kTM)
 };
 
+// Instruction order of one half step, for the scheduler: the NB weight
+// fragment reads, then NMB times (NB MFMAs, one A fragment read).  The MFMAs
+// of a half step use operands read in the previous half step, so each read
+// has the MFMAs issued after it to land.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+template <int I, int N, int NB>
+__device__ __forceinline__ void mfma_read_pairs() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, NB, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    mfma_read_pairs<I + 1, N, NB>();
+  }
+}
+template <int NMB, int NB>
+__device__ __forceinline__ void half_step_order() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NB, 0);
+  mfma_read_pairs<0, NMB, NB>();
+}
+
 // The K loop and epilogue of one tile computing NMB 16-row blocks (a
 // compile-time count, so the MFMA sequence has no data-dependent branches).
-template <int PHASE, int WN, int NMB>
+template <int PHASE, int WN, int NB, int NMB>
 __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) {
-  constexpr int XB = kMB / WN;  // x row blocks loaded by each wavefront
+  static_assert(WN * NB <= kBlocks, "weight blocks per tile");
+  constexpr int XB = kMB / WN;  // A row blocks loaded by each wavefront
+  constexpr int HB = NB / 2;
   const int KT = t.K / kKS;
   // load side: this lane fetches row lr of each 8-row group, chunk lc
   const int lr = lane / 8, lc = (lane % 8) ^ (lane / 8);
-  const uint16_t* wp[2][2];
+  const uint16_t* wp[NB][2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    wp[0][g] = t.w0 + (g * 8 + lr) * t.K + lc * 8;
-    wp[1][g] = t.w1 + (g * 8 + lr) * t.K + lc * 8;
-  }
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      wp[b][g] = (b < HB ? t.wlo : t.whi) + ((b % HB) * 16 + g * 8 + lr) * t.K + lc * 8;
   const uint16_t* xp[XB][2];
 #pragma unroll
   for (int b = 0; b < XB; ++b)
@@ -316,77 +341,99 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   const int pos0 = r8 * 8 + ((0 + lane / 16) ^ r8);
   const int pos1 = r8 * 8 + ((4 + lane / 16) ^ r8);
 
-  f32x4 acc0[NMB], acc1[NMB];
+  f32x4 acc[NB][NMB];
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) {
-    acc0[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[b][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // request K stage KT_ into ST
+  // request K stage KT_ (of the rotated order) into ST
 #define CLE_ISSUE(ST, KT_)                                                          \
   {                                                                                 \
     int kr = (KT_) + t.rot;                                                         \
     kr -= kr >= KT ? KT : 0;                                                        \
     const int ko = kr * kKS;                                                        \
-    _Pragma("unroll") for (int g = 0; g < 2; ++g) {                                 \
-      dma16(wp[0][g] + ko, &ST.w[wave * 2 + 0][g][0]);                              \
-      dma16(wp[1][g] + ko, &ST.w[wave * 2 + 1][g][0]);                              \
-    }                                                                               \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
+      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
+        dma16(wp[b][g] + ko, &ST.w[wave * NB + b][g][0]);                           \
     _Pragma("unroll") for (int b = 0; b < XB; ++b)                                  \
       _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
         dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
   }
-#define CLE_COMPUTE(ST)                                                             \
-  _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                   \
-    const int pos = h == 0 ? pos0 : pos1;                                           \
-    const bf16x8 B0 = __builtin_bit_cast(bf16x8, ST.w[wave * 2 + 0][rg][pos]);      \
-    const bf16x8 B1 = __builtin_bit_cast(bf16x8, ST.w[wave * 2 + 1][rg][pos]);      \
-    _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb) {                            \
-      const bf16x8 Af = __builtin_bit_cast(bf16x8, ST.x[mb][rg][pos]);              \
-      acc0[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B0, acc0[mb], 0, 0, 0); \
-      acc1[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Af, B1, acc1[mb], 0, 0, 0); \
-    }                                                                               \
+  // The operands of one K slice of a stage: NB weight fragments and NMB A
+  // fragments, read from LDS into registers.  Slice 0 and slice 1 have their
+  // own registers.
+  bf16x8 fb[2][NB], fa[2][NMB];
+#define CLE_READ(ST, H)                                                             \
+  {                                                                                 \
+    const int pos = (H) == 0 ? pos0 : pos1;                                         \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
+      fb[H][b] = __builtin_bit_cast(bf16x8, ST.w[wave * NB + b][rg][pos]);          \
+    _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                              \
+      fa[H][mb] = __builtin_bit_cast(bf16x8, ST.x[mb][rg][pos]);                    \
   }
-  // Stage KT_ (in CUR): wait for this wavefront's loads of stage KT_ (those
-  // of the next stage may stay in flight), barrier (every wavefront's loads
-  // of stage KT_ have landed and every wavefront is done with stage KT_-1),
-  // request stage KT_+2 into the buffer of stage KT_-1, compute.  Requests
-  // are unconditional (the stage index is clamped at the end, re-reading the
-  // last stage into a finished buffer) so that every wavefront always has
-  // exactly kPerStep requests per stage in flight and the compiler can tell
-  // which buffer each request writes.
-  constexpr int kPerStep = 4 + 2 * XB;
+#define CLE_MFMA(H)                                                                 \
+  _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                                \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
+      acc[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[H][mb], fb[H][b], acc[b][mb], 0, 0, 0);
+  // Software pipeline by half a stage.  On entry to step KT_ the slice-0
+  // MFMAs of stage KT_ are issued and its slice-1 operands are in registers;
+  // stage KT_ sits in buffer CUR and stage KT_+1 in NXT.  The step waits for
+  // this wavefront's loads of stage KT_+1 (stage KT_+2 may stay in flight),
+  // synchronises (every wavefront's loads of KT_+1 have landed, and every
+  // wavefront has finished reading CUR), requests stage KT_+3 into CUR, then
+  // issues the slice-1 MFMAs of KT_ while reading slice 0 of KT_+1, and the
+  // slice-0 MFMAs of KT_+1 while reading its slice 1, so the LDS reads of a
+  // stage overlap the MFMAs of its neighbours.  Requests are unconditional
+  // (the stage index is clamped at the end, re-reading the last stage into a
+  // finished buffer) so that every wavefront always has exactly kPerStep
+  // requests per stage in flight and the compiler can tell which buffer each
+  // request writes.
+  constexpr int kPerStep = 2 * NB + 2 * XB;
 #define CLE_STEP(CUR, NXT, KT_)                                                     \
   {                                                                                 \
-    wait_vmcnt<kPerStep * (kStages - 2)>();                                         \
+    wait_vmcnt<kPerStep>();                                                         \
     stage_barrier();                                                                \
-    CLE_ISSUE(NXT, min((KT_) + kStages - 1, KT - 1));                               \
-    CLE_COMPUTE(CUR);                                                               \
+    CLE_ISSUE(CUR, min((KT_) + 3, KT - 1));                                         \
+    CLE_MFMA(1);                                                                    \
+    CLE_READ(NXT, 0);                                                               \
+    half_step_order<NMB, NB>();                                                     \
+    CLE_MFMA(0);                                                                    \
+    CLE_READ(NXT, 1);                                                               \
+    half_step_order<NMB, NB>();                                                     \
   }
 
-  auto& st0 = g_st0<PHASE, WN>;
-  auto& st1 = g_st1<PHASE, WN>;
-  auto& st2 = g_st2<PHASE, WN>;
+  static_assert(kStages == 3, "the pipeline below is written for 3 buffers");
+  auto& st0 = g_st0<PHASE, WN, NB>;
+  auto& st1 = g_st1<PHASE, WN, NB>;
+  auto& st2 = g_st2<PHASE, WN, NB>;
   CLE_ISSUE(st0, 0);
   CLE_ISSUE(st1, min(1, KT - 1));
+  CLE_ISSUE(st2, min(2, KT - 1));
+  wait_vmcnt<2 * kPerStep>();
+  stage_barrier();
+  CLE_READ(st0, 0);
+  CLE_MFMA(0);
+  CLE_READ(st0, 1);
   int kt = 0;
-  for (; kt + 3 <= KT; kt += 3) {
-    CLE_STEP(st0, st2, kt);
-    CLE_STEP(st1, st0, kt + 1);
-    CLE_STEP(st2, st1, kt + 2);
+  for (; kt + 3 < KT; kt += 3) {
+    CLE_STEP(st0, st1, kt);
+    CLE_STEP(st1, st2, kt + 1);
+    CLE_STEP(st2, st0, kt + 2);
   }
-  if (kt < KT) {
-    CLE_STEP(st0, st2, kt);
+  if (kt + 1 < KT) {
+    CLE_STEP(st0, st1, kt);
     ++kt;
   }
-  if (kt < KT) {
-    CLE_STEP(st1, st0, kt);
+  if (kt + 1 < KT) {
+    CLE_STEP(st1, st2, kt);
   }
+  CLE_MFMA(1);  // slice 1 of the last stage
 #undef CLE_ISSUE
-#undef CLE_COMPUTE
+#undef CLE_READ
+#undef CLE_MFMA
 #undef CLE_STEP
-  wait_vmcnt<0>();  // the clamped tail requests have landed before buffers are reused
+  wait_vmcnt<0>();  // the clamped requests have landed before buffers are reused
 
   // epilogue: lane holds rows mb*16 + (lane/16)*4 + i, column lane%16 of each block
   const int g4 = lane / 16;
@@ -396,11 +443,14 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
     for (int i = 0; i < 4; ++i) {
       const int row = mb * 16 + g4 * 4 + i;
       if (row < t.nrows) {
+        uint16_t* o = t.out + row * t.ldo + t.col;
         if (PHASE == 1) {
-          t.out[row * t.ldo + t.col] = f32_to_bf16(silu(acc0[mb][i]) * acc1[mb][i]);
+#pragma unroll
+          for (int b = 0; b < HB; ++b)
+            o[b * 16] = f32_to_bf16(silu(acc[b][mb][i]) * acc[HB + b][mb][i]);
         } else {
-          t.out[row * t.ldo + t.col] = f32_to_bf16(acc0[mb][i]);
-          t.out[row * t.ldo + t.col + 16] = f32_to_bf16(acc1[mb][i]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) o[b * 16] = f32_to_bf16(acc[b][mb][i]);
         }
       }
     }
@@ -408,12 +458,13 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   }
 }
 
-template <int PHASE, int WN>
+template <int PHASE, int WN, int NB>
 __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restrict__ segs,
                                                             int nseg,
                                                             const int* __restrict__ totals,
                                                             int H, int I) {
-  static_assert(kMB % WN == 0 && WN <= kMaxWN, "wavefronts per tile");
+  static_assert(kMB % WN == 0 && WN * NB <= kBlocks && NB % 2 == 0, "tile shape");
+  constexpr int HB = NB / 2;
   const int total = totals[PHASE - 1];
   const int grid = gridDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -448,31 +499,31 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
       t.kdiv = 1;
     }
     const uint16_t* W = static_cast<const uint16_t*>(PHASE == 1 ? sg.w13 : sg.w2);
-    int wrow0, wrow1;  // first rows of this wavefront's two weight blocks
+    int wlo, whi;  // first weight rows of this wavefront's two half groups of blocks
     if (PHASE == 1) {
-      wrow0 = nt * (16 * WN) + wave * 16;  // gate rows
-      wrow1 = I + wrow0;                   // up rows of the same act columns
+      wlo = (nt * WN + wave) * (16 * HB);  // gate rows
+      whi = I + wlo;                       // up rows of the same act columns
       t.out = static_cast<uint16_t*>(sg.act) + static_cast<int64_t>(row0) * I;
-      t.col = nt * (16 * WN) + wave * 16 + l16;
+      t.col = wlo + l16;
     } else {
-      wrow0 = nt * (32 * WN) + wave * 32;
-      wrow1 = wrow0 + 16;
+      wlo = (nt * WN + wave) * (16 * NB);
+      whi = wlo + 16 * HB;
       t.out = static_cast<uint16_t*>(sg.y) + static_cast<int64_t>(row0) * H;
-      t.col = nt * (32 * WN) + wave * 32 + l16;
+      t.col = wlo + l16;
     }
     t.ldo = ldo;
-    t.w0 = W + static_cast<int64_t>(wrow0) * K;
-    t.w1 = W + static_cast<int64_t>(wrow1) * K;
+    t.wlo = W + static_cast<int64_t>(wlo) * K;
+    t.whi = W + static_cast<int64_t>(whi) * K;
     const int nmb = (t.nrows + 15) / 16;
     switch (nmb) {
-      case 1: tile_nmb<PHASE, WN, 1>(t, wave, lane); break;
-      case 2: tile_nmb<PHASE, WN, 2>(t, wave, lane); break;
-      case 3: tile_nmb<PHASE, WN, 3>(t, wave, lane); break;
-      case 4: tile_nmb<PHASE, WN, 4>(t, wave, lane); break;
-      case 5: tile_nmb<PHASE, WN, 5>(t, wave, lane); break;
-      case 6: tile_nmb<PHASE, WN, 6>(t, wave, lane); break;
-      case 7: tile_nmb<PHASE, WN, 7>(t, wave, lane); break;
-      default: tile_nmb<PHASE, WN, 8>(t, wave, lane); break;
+      case 1: tile_nmb<PHASE, WN, NB, 1>(t, wave, lane); break;
+      case 2: tile_nmb<PHASE, WN, NB, 2>(t, wave, lane); break;
+      case 3: tile_nmb<PHASE, WN, NB, 3>(t, wave, lane); break;
+      case 4: tile_nmb<PHASE, WN, NB, 4>(t, wave, lane); break;
+      case 5: tile_nmb<PHASE, WN, NB, 5>(t, wave, lane); break;
+      case 6: tile_nmb<PHASE, WN, NB, 6>(t, wave, lane); break;
+      case 7: tile_nmb<PHASE, WN, NB, 7>(t, wave, lane); break;
+      default: tile_nmb<PHASE, WN, NB, 8>(t, wave, lane); break;
     }
     // every wavefront is done reading the stages before the next tile's
     // first requests overwrite them
@@ -557,14 +608,15 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
   if (!d || n_desc < 1 || n_desc > CLE_MAX_DESC) return CLE_EINVAL;
   if (!w13 || !w2 || L < 1 || E < 1 || E > CLE_MAX_E || n_shared < 0) return CLE_EINVAL;
   if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
-  // bf16: 256-row tiles of WN wavefronts (16*WN act columns, 32*WN output
-  // columns); WN = 8 when the shape allows it, else 4.  f32: 64 x 64 tiles.
+  // bf16: 128-row tiles of 16 weight blocks (8 wavefronts x 2; 128 act
+  // columns, 256 output columns) when the shape allows it, else of 8 blocks
+  // (4 wavefronts x 2).  f32: 64 x 64 tiles.
   if (I < 64 || I % 64) return CLE_EINVAL;
   if (dt == CLE_BF16 ? (H < 128 || H % 128) : (H < 64 || H % 64)) return CLE_EINVAL;
-  const int wn = (dt == CLE_BF16 && I % 128 == 0 && H % 256 == 0) ? 8 : 4;
+  const bool wide = dt == CLE_BF16 && I % 128 == 0 && H % 256 == 0;
   const int tm = dt == CLE_BF16 ? kTM : kBM;
-  const int tn1 = dt == CLE_BF16 ? 16 * wn : kBNF;
-  const int tn2 = dt == CLE_BF16 ? 32 * wn : kBNF;
+  const int tn1 = dt == CLE_BF16 ? (wide ? 128 : 64) : kBNF;
+  const int tn2 = dt == CLE_BF16 ? (wide ? 256 : 128) : kBNF;
   if (n_shared > 0 && (!w13_shared || !w2_shared)) return CLE_EINVAL;
   const int esz = dt == CLE_BF16 ? 2 : 4;
   if (!aligned(w13, 16) || !aligned(w2, 16)) return CLE_EINVAL;
@@ -626,12 +678,12 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
     return CLE_EHIP;
   static int occ_b1[64], occ_b2[64], occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64];
   if (ub1 > 0) {
-    if (dt == CLE_BF16 && wn == 8) {
-      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8>, occ_b1, 512));
-      ffn_gemm_bf16<1, 8><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+    if (wide) {
+      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8, 2>, occ_b1, 512));
+      ffn_gemm_bf16<1, 8, 2><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
     } else if (dt == CLE_BF16) {
-      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4>, occ_c1, 256));
-      ffn_gemm_bf16<1, 4><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4, 2>, occ_c1, 256));
+      ffn_gemm_bf16<1, 4, 2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
     } else {
       const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_f32<1>, occ_f1, 256));
       ffn_gemm_f32<1><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
@@ -640,12 +692,12 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
   if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[1]), s) != hipSuccess)
     return CLE_EHIP;
   if (ub2 > 0) {
-    if (dt == CLE_BF16 && wn == 8) {
-      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8>, occ_b2, 512));
-      ffn_gemm_bf16<2, 8><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+    if (wide) {
+      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8, 2>, occ_b2, 512));
+      ffn_gemm_bf16<2, 8, 2><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
     } else if (dt == CLE_BF16) {
-      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4>, occ_c2, 256));
-      ffn_gemm_bf16<2, 4><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4, 2>, occ_c2, 256));
+      ffn_gemm_bf16<2, 4, 2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
     } else {
       const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_f32<2>, occ_f2, 256));
       ffn_gemm_f32<2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
