@@ -21,7 +21,7 @@ OK, EINVAL, EHIP, EWORKSPACE, EUNSUPPORTED = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
 POLICY_B0_ALONE, POLICY_B1_LOCKSTEP, POLICY_CUMUTIL, POLICY_MAXUTIL, POLICY_DIFFPEAK = range(5)
 POLICIES = {"b0": 0, "b1": 1, "cumutil": 2, "maxutil": 3, "diffpeak": 4}
-OP_DISPATCH, OP_FFN = 1, 2
+OP_DISPATCH, OP_FFN, OP_DISPATCH_MANY = 1, 2, 3
 MAX_E, MAX_MICROBATCHES, MAX_MAXUTIL_POOL, MAX_DESC = 1024, 64, 20, 64
 
 
@@ -56,6 +56,11 @@ class FfnDesc(ctypes.Structure):
 
 _sig = {
     "cle_route": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "cle_route_many": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "cle_dispatch_many": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
+                                 _vp]),
+    "cle_combine_many": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp,
+                                _i32, _vp]),
     "cle_dispatch": (_i32, [_vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                             _vp, _sz, _vp]),
     "cle_grouped_expert_ffn": (_i32, [ctypes.POINTER(FfnDesc), _i32, _vp, _vp, _vp, _vp, _i32,
@@ -128,6 +133,41 @@ def dispatch(topk_idx, E, x, counts, offsets, dest, src, xp, ws, stream=None):
     _check("cle_dispatch", _lib.cle_dispatch(
         _ptr(topk_idx), T, k, E, _ptr(x), H, _dt(x), _ptr(counts), _ptr(offsets), _ptr(dest),
         _ptr(src), _ptr(xp), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def _ptrs(ts):
+    """HOST array of device addresses (None -> NULL), kept alive by the caller's
+    reference to the returned ctypes array for the duration of the call."""
+    return (_vp * len(ts))(*[None if t is None else t.data_ptr() for t in ts])
+
+
+def route_many(logits, k, topk_idx, topk_gate, stream=None):
+    """logits, topk_idx, topk_gate: equal-length lists of per-micro-batch tensors."""
+    n = len(logits)
+    T, E = logits[0].shape
+    _check("cle_route_many", _lib.cle_route_many(
+        n, _ptrs(logits), T, E, k, _ptrs(topk_idx), _ptrs(topk_gate), _stream(stream)))
+
+
+def dispatch_many(topk_idx, E, counts, offsets, dest, src, ws, stream=None):
+    """Per-micro-batch lists; no row copy (the expert launch reads rows through src)."""
+    n = len(topk_idx)
+    T, k = topk_idx[0].shape
+    _check("cle_dispatch_many", _lib.cle_dispatch_many(
+        n, _ptrs(topk_idx), T, k, E, _ptrs(counts), _ptrs(offsets), _ptrs(dest), _ptrs(src),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def combine_many(yp, dest, topk_gate, y, y_shared=None, residual=None, stream=None):
+    """Per-micro-batch lists; y_shared / residual: None or lists (entries may be None)."""
+    n = len(yp)
+    T, k = topk_gate[0].shape
+    H = y[0].shape[-1]
+    ns = 0 if y_shared is None or y_shared[0] is None else y_shared[0].shape[0]
+    _check("cle_combine_many", _lib.cle_combine_many(
+        n, _ptrs(yp), _ptrs(dest), _ptrs(topk_gate), T, k, H,
+        None if y_shared is None else _ptrs(y_shared), ns,
+        None if residual is None else _ptrs(residual), _ptrs(y), _dt(y[0]), _stream(stream)))
 
 
 def make_desc(layer, rows, offsets, xp, act, yp, shared_rows=0, x_shared=None, act_shared=None,

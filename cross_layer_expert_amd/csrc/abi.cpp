@@ -42,12 +42,15 @@ static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 extern "C" size_t cle_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t k,
                                       int32_t n_shared, int32_t n_desc) {
-  if (op == CLE_OP_DISPATCH) {
+  if (op == CLE_OP_DISPATCH || op == CLE_OP_DISPATCH_MANY) {
     if (T < 0 || k < 1 || E < 1 || E > CLE_MAX_E) return 0;
     int64_t A = static_cast<int64_t>(T) * k;
     int64_t chunks = cle::dispatch_chunks(A);
     if (chunks < 1) chunks = 1;
-    return round_up(static_cast<size_t>(chunks) * E * sizeof(int32_t), 256);
+    const size_t one = round_up(static_cast<size_t>(chunks) * E * sizeof(int32_t), 256);
+    if (op == CLE_OP_DISPATCH) return one;
+    if (n_desc < 1 || n_desc > CLE_MAX_MICROBATCHES) return 0;
+    return one * static_cast<size_t>(n_desc);
   }
   if (op == CLE_OP_FFN) {
     if (E < 1 || E > CLE_MAX_E || n_shared < 0 || n_desc < 1 || n_desc > CLE_MAX_DESC) return 0;

@@ -49,16 +49,29 @@ struct Vec<float> {
   }
 };
 
+// Buffers of the micro-batches of one launch (blockIdx.y picks one).
+struct CombineArgs {
+  const void* yp[CLE_MAX_MICROBATCHES];
+  const int* dest[CLE_MAX_MICROBATCHES];
+  const float* gate[CLE_MAX_MICROBATCHES];
+  const void* y_shared[CLE_MAX_MICROBATCHES];
+  const void* residual[CLE_MAX_MICROBATCHES];
+  void* y[CLE_MAX_MICROBATCHES];
+};
+
 // KMAX > 0: k <= KMAX slots, whose destinations and gates are held in
 // registers so that all slot rows of a column chunk are requested before the
 // first one is used.  KMAX == 0: any k, one slot at a time.  Both sum the
 // slots in order 0..k-1.
 template <typename T, int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp,
-                                                      const int* __restrict__ dest,
-                                                      const float* __restrict__ gate, int T_,
-                                                      int k, int H, const T* __restrict__ y_shared,
-                                                      int n_shared, const T* residual, T* y) {
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs args, int T_, int k, int H,
+                                                      int n_shared) {
+  const T* __restrict__ yp = static_cast<const T*>(args.yp[blockIdx.y]);
+  const int* __restrict__ dest = args.dest[blockIdx.y];
+  const float* __restrict__ gate = args.gate[blockIdx.y];
+  const T* __restrict__ y_shared = static_cast<const T*>(args.y_shared[blockIdx.y]);
+  const T* residual = static_cast<const T*>(args.residual[blockIdx.y]);
+  T* y = static_cast<T*>(args.y[blockIdx.y]);
   constexpr int N = Vec<T>::N;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -118,12 +131,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yp,
 }
 
 template <typename T>
-void launch_combine(dim3 grid, hipStream_t s, const T* yp, const int* dest, const float* gate,
-                    int T_, int k, int H, const T* ysh, int ns, const T* res, T* y) {
+void launch_combine(const CombineArgs& a, int n, int T_, int k, int H, int ns, hipStream_t s) {
+  const dim3 grid((T_ + 3) / 4, n);
   if (k <= 8)
-    combine_kernel<T, 8><<<grid, dim3(256), 0, s>>>(yp, dest, gate, T_, k, H, ysh, ns, res, y);
+    combine_kernel<T, 8><<<grid, dim3(256), 0, s>>>(a, T_, k, H, ns);
   else
-    combine_kernel<T, 0><<<grid, dim3(256), 0, s>>>(yp, dest, gate, T_, k, H, ysh, ns, res, y);
+    combine_kernel<T, 0><<<grid, dim3(256), 0, s>>>(a, T_, k, H, ns);
 }
 
 }  // namespace
@@ -133,24 +146,42 @@ extern "C" cle_status cle_combine(const void* yp, const int32_t* dest, const flo
                                   int32_t T, int32_t k, int32_t H, const void* y_shared,
                                   int32_t n_shared, const void* residual, void* y, cle_dtype dt,
                                   void* stream) {
+  return cle_combine_many(1, &yp, &dest, &topk_gate, T, k, H, &y_shared, n_shared, &residual, &y,
+                          dt, stream);
+}
+
+extern "C" cle_status cle_combine_many(int32_t n, const void* const* yp,
+                                       const int32_t* const* dest,
+                                       const float* const* topk_gate, int32_t T, int32_t k,
+                                       int32_t H, const void* const* y_shared, int32_t n_shared,
+                                       const void* const* residual, void* const* y, cle_dtype dt,
+                                       void* stream) {
   using namespace cle;
+  if (n < 1 || n > CLE_MAX_MICROBATCHES || !yp || !dest || !topk_gate || !y) return CLE_EINVAL;
   if (T < 0 || k < 1 || H < 8 || H % 8 || n_shared < 0) return CLE_EINVAL;
   if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
   if (T == 0) return CLE_OK;
-  if (!yp || !dest || !topk_gate || !y) return CLE_EINVAL;
   if (n_shared > 0 && !y_shared) return CLE_EINVAL;
-  if (!aligned(yp, 16) || !aligned(y, 16) || (y_shared && !aligned(y_shared, 16)) ||
-      (residual && !aligned(residual, 16)))
-    return CLE_EINVAL;
-  const dim3 grid((T + 3) / 4);
+  CombineArgs a;
+  for (int j = 0; j < n; ++j) {
+    const void* ys = y_shared ? y_shared[j] : nullptr;
+    const void* res = residual ? residual[j] : nullptr;
+    if (!yp[j] || !dest[j] || !topk_gate[j] || !y[j]) return CLE_EINVAL;
+    if (n_shared > 0 && !ys) return CLE_EINVAL;
+    if (!aligned(yp[j], 16) || !aligned(y[j], 16) || (ys && !aligned(ys, 16)) ||
+        (res && !aligned(res, 16)))
+      return CLE_EINVAL;
+    a.yp[j] = yp[j];
+    a.dest[j] = dest[j];
+    a.gate[j] = topk_gate[j];
+    a.y_shared[j] = ys;
+    a.residual[j] = res;
+    a.y[j] = y[j];
+  }
   hipStream_t s = as_stream(stream);
   if (dt == CLE_BF16)
-    launch_combine<uint16_t>(grid, s, static_cast<const uint16_t*>(yp), dest, topk_gate, T, k, H,
-                             static_cast<const uint16_t*>(y_shared), n_shared,
-                             static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(y));
+    launch_combine<uint16_t>(a, n, T, k, H, n_shared, s);
   else
-    launch_combine<float>(grid, s, static_cast<const float*>(yp), dest, topk_gate, T, k, H,
-                          static_cast<const float*>(y_shared), n_shared,
-                          static_cast<const float*>(residual), static_cast<float*>(y));
+    launch_combine<float>(a, n, T, k, H, n_shared, s);
   return launch_status();
 }

@@ -22,8 +22,21 @@ namespace {
 constexpr int kChunkWaves = 4;
 constexpr int kPerWave = kDispatchChunk / kChunkWaves;  // 256 assignments per wave
 
-__global__ __launch_bounds__(256) void dispatch_count(const int* __restrict__ idx, int64_t A,
-                                                      int E, int* __restrict__ chunk_hist) {
+// Buffers of the micro-batches of one launch (blockIdx.y picks one); each has
+// its own chunk-histogram region of the workspace, hist_stride ints apart.
+struct DispatchArgs {
+  const int* idx[CLE_MAX_MICROBATCHES];
+  int* counts[CLE_MAX_MICROBATCHES];
+  int* offsets[CLE_MAX_MICROBATCHES];
+  int* dest[CLE_MAX_MICROBATCHES];
+  int* src[CLE_MAX_MICROBATCHES];
+  int* hist;
+  int64_t hist_stride;
+};
+
+__global__ __launch_bounds__(256) void dispatch_count(DispatchArgs args, int64_t A, int E) {
+  const int* __restrict__ idx = args.idx[blockIdx.y];
+  int* __restrict__ chunk_hist = args.hist + blockIdx.y * args.hist_stride;
   __shared__ int hist[CLE_MAX_E];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
@@ -42,10 +55,12 @@ __global__ __launch_bounds__(256) void dispatch_count(const int* __restrict__ id
 
 // Turns chunk counts into absolute chunk bases in place and writes counts
 // and offsets.
-__global__ __launch_bounds__(1024) void dispatch_scan(int* __restrict__ chunk_hist, int64_t chunks,
-                                                      int E, int64_t A, int* __restrict__ counts,
-                                                      int* __restrict__ offsets,
-                                                      int* __restrict__ src) {
+__global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs args, int64_t chunks, int E,
+                                                      int64_t A) {
+  int* __restrict__ chunk_hist = args.hist + blockIdx.x * args.hist_stride;
+  int* __restrict__ counts = args.counts[blockIdx.x];
+  int* __restrict__ offsets = args.offsets[blockIdx.x];
+  int* __restrict__ src = args.src[blockIdx.x];
   __shared__ int tot[CLE_MAX_E];
   __shared__ int part[1024];
   const int tid = threadIdx.x;
@@ -85,11 +100,12 @@ __global__ __launch_bounds__(1024) void dispatch_scan(int* __restrict__ chunk_hi
     for (int64_t c = 0; c < chunks; ++c) chunk_hist[c * E + e] += tot[e];
 }
 
-__global__ __launch_bounds__(256) void dispatch_scatter(const int* __restrict__ idx, int64_t A,
-                                                        int E, int id_bits,
-                                                        const int* __restrict__ chunk_base,
-                                                        int* __restrict__ dest,
-                                                        int* __restrict__ src) {
+__global__ __launch_bounds__(256) void dispatch_scatter(DispatchArgs args, int64_t A, int E,
+                                                        int id_bits) {
+  const int* __restrict__ idx = args.idx[blockIdx.y];
+  const int* __restrict__ chunk_base = args.hist + blockIdx.y * args.hist_stride;
+  int* __restrict__ dest = args.dest[blockIdx.y];
+  int* __restrict__ src = args.src[blockIdx.y];
   __shared__ int wcount[kChunkWaves][CLE_MAX_E];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -179,6 +195,25 @@ __global__ __launch_bounds__(256) void dispatch_gather(const T* __restrict__ x, 
 }  // namespace
 }  // namespace cle
 
+namespace cle {
+namespace {
+
+// count, scan and scatter for n micro-batches of A assignments each
+cle_status launch_dispatch(const DispatchArgs& a, int n, int64_t A, int E, hipStream_t s) {
+  const int64_t chunks = dispatch_chunks(A);
+  if (chunks > 0)
+    dispatch_count<<<dim3(static_cast<unsigned>(chunks), n), dim3(256), 0, s>>>(a, A, E);
+  dispatch_scan<<<dim3(n), dim3(1024), 0, s>>>(a, chunks, E, A);
+  if (A == 0) return launch_status();
+  int id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  dispatch_scatter<<<dim3(static_cast<unsigned>(chunks), n), dim3(256), 0, s>>>(a, A, E, id_bits);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace cle
+
 extern "C" cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
                                    const void* x, int32_t H, cle_dtype dt, int32_t* counts,
                                    int32_t* offsets, int32_t* dest, int32_t* src, void* xp,
@@ -195,18 +230,16 @@ extern "C" cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k
   const size_t need = cle_workspace_bytes(CLE_OP_DISPATCH, T, E, k, 0, 1);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return CLE_EWORKSPACE;
   hipStream_t s = as_stream(stream);
-  int64_t chunks = dispatch_chunks(A);
-  int* hist = static_cast<int*>(ws);
-  if (chunks > 0) {
-    dispatch_count<<<dim3(static_cast<unsigned>(chunks)), dim3(256), 0, s>>>(topk_idx, A, E, hist);
-  }
-  dispatch_scan<<<dim3(1), dim3(1024), 0, s>>>(hist, chunks, E, A, counts, offsets, src);
-  if (A == 0) return launch_status();
-  int id_bits = 0;
-  while ((1 << id_bits) < E) ++id_bits;
-  dispatch_scatter<<<dim3(static_cast<unsigned>(chunks)), dim3(256), 0, s>>>(
-      topk_idx, A, E, id_bits, hist, dest, src);
-  if (!xp) return launch_status();
+  DispatchArgs a;
+  a.idx[0] = topk_idx;
+  a.counts[0] = counts;
+  a.offsets[0] = offsets;
+  a.dest[0] = dest;
+  a.src[0] = src;
+  a.hist = static_cast<int*>(ws);
+  a.hist_stride = 0;
+  const cle_status st = launch_dispatch(a, 1, A, E, s);
+  if (st != CLE_OK || A == 0 || !xp) return st;
   const dim3 ggrid(static_cast<unsigned>((A + 3) / 4));
   if (dt == CLE_BF16)
     dispatch_gather<uint16_t><<<ggrid, dim3(256), 0, s>>>(
@@ -215,4 +248,33 @@ extern "C" cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k
     dispatch_gather<float><<<ggrid, dim3(256), 0, s>>>(static_cast<const float*>(x), A, k, H,
                                                        offsets, E, src, static_cast<float*>(xp));
   return launch_status();
+}
+
+extern "C" cle_status cle_dispatch_many(int32_t n, const int32_t* const* topk_idx, int32_t T,
+                                        int32_t k, int32_t E, int32_t* const* counts,
+                                        int32_t* const* offsets, int32_t* const* dest,
+                                        int32_t* const* src, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  using namespace cle;
+  if (n < 1 || n > CLE_MAX_MICROBATCHES || !topk_idx || !counts || !offsets || !dest || !src)
+    return CLE_EINVAL;
+  if (T < 0 || k < 1 || E < 1 || E > CLE_MAX_E) return CLE_EINVAL;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (A > INT32_MAX) return CLE_EUNSUPPORTED;
+  DispatchArgs a;
+  for (int j = 0; j < n; ++j) {
+    if (!counts[j] || !offsets[j]) return CLE_EINVAL;
+    if (A > 0 && (!topk_idx[j] || !dest[j] || !src[j])) return CLE_EINVAL;
+    a.idx[j] = topk_idx[j];
+    a.counts[j] = counts[j];
+    a.offsets[j] = offsets[j];
+    a.dest[j] = dest[j];
+    a.src[j] = src[j];
+  }
+  const size_t one = cle_workspace_bytes(CLE_OP_DISPATCH, T, E, k, 0, 1);
+  const size_t need = cle_workspace_bytes(CLE_OP_DISPATCH_MANY, T, E, k, 0, n);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return CLE_EWORKSPACE;
+  a.hist = static_cast<int*>(ws);
+  a.hist_stride = static_cast<int64_t>(one / sizeof(int));
+  return launch_dispatch(a, n, A, E, as_stream(stream));
 }

@@ -14,6 +14,13 @@ namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread block
 
+// Buffers of the micro-batches of one launch (blockIdx.y picks one).
+struct RouteArgs {
+  const float* logits[CLE_MAX_MICROBATCHES];
+  int* idx[CLE_MAX_MICROBATCHES];
+  float* gate[CLE_MAX_MICROBATCHES];
+};
+
 __device__ __forceinline__ uint32_t ord_bits(float z) {
   if (z == 0.0f) z = 0.0f;  // -0.0 and +0.0 are the same logit
   uint32_t b = __float_as_uint(z);
@@ -37,9 +44,10 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 template <int VPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
-                                                    int E, int k, int* __restrict__ idx,
-                                                    float* __restrict__ gate) {
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E, int k) {
+  const float* __restrict__ logits = args.logits[blockIdx.y];
+  int* __restrict__ idx = args.idx[blockIdx.y];
+  float* __restrict__ gate = args.gate[blockIdx.y];
   __shared__ float zsel[kRouteWaves][CLE_MAX_E];
   __shared__ int esel[kRouteWaves][CLE_MAX_E];
   const int wave = threadIdx.x / kWave;
@@ -90,24 +98,46 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 }  // namespace
 }  // namespace cle
 
-extern "C" cle_status cle_route(const float* logits, int32_t T, int32_t E, int32_t k,
-                                int32_t* topk_idx, float* topk_gate, void* stream) {
-  using namespace cle;
-  if (T < 0 || E < 1 || E > CLE_MAX_E || k < 1 || k > E) return CLE_EINVAL;
-  if (T == 0) return CLE_OK;
-  if (!logits || !topk_idx || !topk_gate) return CLE_EINVAL;
-  const dim3 grid((T + kRouteWaves - 1) / kRouteWaves), block(256);
-  hipStream_t s = as_stream(stream);
+namespace cle {
+namespace {
+
+cle_status launch_route(const RouteArgs& a, int n, int T, int E, int k, hipStream_t s) {
+  const dim3 grid((T + kRouteWaves - 1) / kRouteWaves, n), block(256);
   const int vpl = (E + kWave - 1) / kWave;
   if (vpl <= 1)
-    route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+    route_kernel<1><<<grid, block, 0, s>>>(a, T, E, k);
   else if (vpl <= 2)
-    route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+    route_kernel<2><<<grid, block, 0, s>>>(a, T, E, k);
   else if (vpl <= 4)
-    route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+    route_kernel<4><<<grid, block, 0, s>>>(a, T, E, k);
   else if (vpl <= 8)
-    route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+    route_kernel<8><<<grid, block, 0, s>>>(a, T, E, k);
   else
-    route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, topk_idx, topk_gate);
+    route_kernel<16><<<grid, block, 0, s>>>(a, T, E, k);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace cle
+
+extern "C" cle_status cle_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                                int32_t* topk_idx, float* topk_gate, void* stream) {
+  return cle_route_many(1, &logits, T, E, k, &topk_idx, &topk_gate, stream);
+}
+
+extern "C" cle_status cle_route_many(int32_t n, const float* const* logits, int32_t T, int32_t E,
+                                     int32_t k, int32_t* const* topk_idx,
+                                     float* const* topk_gate, void* stream) {
+  using namespace cle;
+  if (n < 1 || n > CLE_MAX_MICROBATCHES || !logits || !topk_idx || !topk_gate) return CLE_EINVAL;
+  if (T < 0 || E < 1 || E > CLE_MAX_E || k < 1 || k > E) return CLE_EINVAL;
+  if (T == 0) return CLE_OK;
+  RouteArgs a;
+  for (int j = 0; j < n; ++j) {
+    if (!logits[j] || !topk_idx[j] || !topk_gate[j]) return CLE_EINVAL;
+    a.logits[j] = logits[j];
+    a.idx[j] = topk_idx[j];
+    a.gate[j] = topk_gate[j];
+  }
+  return launch_route(a, n, T, E, k, as_stream(stream));
 }

@@ -19,8 +19,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BF16, OP_DISPATCH, OP_FFN, combine, dispatch, grouped_expert_ffn, ids_of,
-               make_desc, mask_of, route, schedule_step_raw, workload_stats, workspace_bytes)
+from . import (BF16, OP_DISPATCH, OP_DISPATCH_MANY, OP_FFN, combine, combine_many, dispatch,
+               dispatch_many, grouped_expert_ffn, ids_of, make_desc, mask_of, route, route_many,
+               schedule_step_raw, workload_stats, workspace_bytes)
 
 
 class Engine:
@@ -31,7 +32,7 @@ class Engine:
     """
 
     def __init__(self, weights, logits, h0, D, k, policy, m, start_layers=None, stream=None,
-                 fused_gather=True):
+                 fused_gather=True, batched=True):
         self.w13, self.w2, self.w13s, self.w2s = weights
         self.L, self.E, I2, self.H = self.w13.shape
         self.I = I2 // 2
@@ -55,6 +56,9 @@ class Engine:
         # fused_gather: the expert launch reads token rows through src, so the
         # expert-sorted copy xp is never materialised
         self.fused = fused_gather
+        # batched: route, dispatch and combine of a whole RunSet in one call
+        # each (needs fused_gather: the batched dispatch copies no rows)
+        self.batched = batched and fused_gather
         self.xp = None if fused_gather else torch.empty((n, A, H), dtype=dt, device=dev)
         self.act = torch.empty((n, A, I), dtype=dt, device=dev)
         self.yp = torch.empty((n, A, H), dtype=dt, device=dev)
@@ -67,7 +71,8 @@ class Engine:
         self.acc = torch.zeros(4, dtype=torch.int64, device=dev)
         self.w_host = torch.zeros((n, D), dtype=torch.int32).pin_memory()
         self.ws_dispatch = torch.empty(
-            max(256, workspace_bytes(OP_DISPATCH, T, E, k)) // 4, dtype=torch.int32, device=dev)
+            max(256, workspace_bytes(OP_DISPATCH_MANY, T, E, k, 0, n)) // 4, dtype=torch.int32,
+            device=dev)
         self.ws_ffn = torch.empty(
             max(256, workspace_bytes(OP_FFN, 0, E, 1, self.ns, n)) // 4, dtype=torch.int32,
             device=dev)
@@ -109,6 +114,17 @@ class Engine:
         dispatch(self.idx[j], self.E, self.h[j], self.counts[j], self.offsets[j], self.dest[j],
                  self.src[j], None if self.fused else self.xp[j], self.ws_dispatch, stream=s)
 
+    def route_dispatch_many(self, js):
+        """AttnRouteDispatch for the micro-batches js, each at its current layer,
+        one launch per pass."""
+        s = self.stream
+        idx = [self.idx[j] for j in js]
+        route_many([self.logits[j, self.l[j]] for j in js], self.k, idx,
+                   [self.gates[j] for j in js], stream=s)
+        dispatch_many(idx, self.E, [self.counts[j] for j in js], [self.offsets[j] for j in js],
+                      [self.dest[j] for j in js], [self.src[j] for j in js], self.ws_dispatch,
+                      stream=s)
+
     def schedule(self) -> list:
         """Workloads to the host, then Schedule(S, m) in the host library."""
         s = self.stream
@@ -131,6 +147,12 @@ class Engine:
             descs.append(d)
         grouped_expert_ffn(descs, self.w13, self.w2, self.ws_ffn, self.w13s, self.w2s,
                            events=events, stream=s)
+        if self.batched:
+            combine_many([self.yp[j] for j in R], [self.dest[j] for j in R],
+                         [self.gates[j] for j in R], [self.h[j] for j in R],
+                         y_shared=None if self.y_sh is None else [self.y_sh[j] for j in R],
+                         residual=[self.h[j] for j in R], stream=s)
+            return
         for j in R:
             combine(self.yp[j], self.dest[j], self.gates[j], self.h[j],
                     y_shared=None if self.y_sh is None else self.y_sh[j], residual=self.h[j],
@@ -138,8 +160,11 @@ class Engine:
 
     def step(self, events=None) -> list:
         """One iteration of the Algorithm 1 loop; returns RunSet_i."""
-        for j in self.prev:
-            if self.l[j] < self.L:
+        todo = [j for j in self.prev if self.l[j] < self.L]
+        if self.batched and todo:
+            self.route_dispatch_many(todo)
+        else:
+            for j in todo:
                 self.route_dispatch(j)
         R = self.schedule()
         layers = [self.l[j] for j in R]

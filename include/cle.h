@@ -58,7 +58,7 @@ typedef enum {
 } cle_policy;
 
 /* Workspace-owning operations, for cle_workspace_bytes(). */
-typedef enum { CLE_OP_DISPATCH = 1, CLE_OP_FFN = 2 } cle_op;
+typedef enum { CLE_OP_DISPATCH = 1, CLE_OP_FFN = 2, CLE_OP_DISPATCH_MANY = 3 } cle_op;
 
 /* Library limits. */
 #define CLE_MAX_E 1024            /* experts per layer */
@@ -80,6 +80,18 @@ typedef enum { CLE_OP_DISPATCH = 1, CLE_OP_FFN = 2 } cle_op;
  */
 cle_status cle_route(const float* logits, int32_t T, int32_t E, int32_t k,
                      int32_t* topk_idx, float* topk_gate, void* stream);
+
+/*
+ * cle_route_many -- cle_route for n micro-batches of T tokens each, in one
+ * launch (Algorithm 1 routes every micro-batch of the previous RunSet).
+ *   logits, topk_idx, topk_gate: HOST arrays of n device pointers, entry j
+ *   laid out as in cle_route.  Results are those of n cle_route calls.
+ * Requires 1 <= n <= CLE_MAX_MICROBATCHES and cle_route's conditions; a NULL
+ * entry (when T > 0) returns CLE_EINVAL before anything is enqueued.
+ */
+cle_status cle_route_many(int32_t n, const float* const* logits, int32_t T, int32_t E,
+                          int32_t k, int32_t* const* topk_idx, float* const* topk_gate,
+                          void* stream);
 
 /*
  * cle_dispatch -- per-expert histogram, exclusive scan, stable permutation
@@ -106,6 +118,22 @@ cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E
                         const void* x, int32_t H, cle_dtype dt,
                         int32_t* counts, int32_t* offsets, int32_t* dest, int32_t* src,
                         void* xp, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * cle_dispatch_many -- counts, offsets, dest and src of cle_dispatch for n
+ * micro-batches of T tokens each, one launch per pass.  No row copy: the
+ * expert launch reads the rows through src (cle_ffn_desc.x / .src).
+ *   topk_idx, counts, offsets, dest, src: HOST arrays of n device pointers,
+ *   entry j laid out as in cle_dispatch.
+ *   ws: at least cle_workspace_bytes(CLE_OP_DISPATCH_MANY, T, E, k, 0, n) bytes,
+ *   256-byte aligned (one cle_dispatch workspace per micro-batch).
+ * Results are those of n cle_dispatch calls.  Requires 1 <= n <=
+ * CLE_MAX_MICROBATCHES, 1 <= k, 1 <= E <= CLE_MAX_E.
+ */
+cle_status cle_dispatch_many(int32_t n, const int32_t* const* topk_idx, int32_t T, int32_t k,
+                             int32_t E, int32_t* const* counts, int32_t* const* offsets,
+                             int32_t* const* dest, int32_t* const* src, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /*
  * One micro-batch of a grouped expert launch.  `layer` selects that layer's
@@ -149,8 +177,9 @@ typedef struct {
  *   phase_events: NULL, or HOST array of 3 hipEvent_t recorded on `stream`
  *              after the planning kernel, after the gate/up phase and after
  *              the down phase (for measurement).
- * Rows of each segment are computed with one fixed instruction sequence, so
- * a row's result does not depend on the other segments in the launch.
+ * Rows of each segment are computed with one fixed instruction sequence and
+ * a K order that depends only on the segment's layer and expert, so a row's
+ * result does not depend on the other segments in the launch.
  * Requires I % 64 == 0, and H % 128 == 0 for bf16 or H % 64 == 0 for f32.
  */
 cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_desc,
@@ -176,6 +205,21 @@ cle_status cle_combine(const void* yp, const int32_t* dest, const float* topk_ga
                        int32_t T, int32_t k, int32_t H,
                        const void* y_shared, int32_t n_shared, const void* residual,
                        void* y, cle_dtype dt, void* stream);
+
+/*
+ * cle_combine_many -- cle_combine for n micro-batches of T tokens each, in
+ * one launch (MoECompute_Combine of Algorithm 1 for a whole RunSet).
+ *   yp, dest, topk_gate, y: HOST arrays of n device pointers, entry j laid
+ *   out as in cle_combine.  y_shared, residual: HOST arrays of n device
+ *   pointers (entries may be NULL as in cle_combine), or NULL for none.
+ * Entry j of y may alias entry j of residual only.  Results are those of n
+ * cle_combine calls.  Requires 1 <= n <= CLE_MAX_MICROBATCHES, H % 8 == 0.
+ */
+cle_status cle_combine_many(int32_t n, const void* const* yp, const int32_t* const* dest,
+                            const float* const* topk_gate, int32_t T, int32_t k, int32_t H,
+                            const void* const* y_shared, int32_t n_shared,
+                            const void* const* residual, void* const* y, cle_dtype dt,
+                            void* stream);
 
 /*
  * cle_workload_stats -- per-group workloads and their step statistics.
@@ -223,6 +267,7 @@ cle_status cle_schedule_step(const int32_t* w, int32_t n, int32_t D, uint64_t re
 /*
  * cle_workspace_bytes -- device workspace, in bytes, that `op` needs:
  *   CLE_OP_DISPATCH: depends on T, E, k (n_shared, n_desc ignored);
+ *   CLE_OP_DISPATCH_MANY: n_desc (= n of cle_dispatch_many) times that;
  *   CLE_OP_FFN:      depends on E, n_shared, n_desc (T, k ignored).
  * The workspace must be 256-byte aligned.  Returns 0 for an unknown op or
  * out-of-range sizes.

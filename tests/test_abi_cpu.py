@@ -21,7 +21,8 @@ def test_every_declared_symbol_is_exported():
     declared = set(re.findall(r"^\s*(?:cle_status|size_t|const char\*)\s+(cle_\w+)\s*\(", text,
                               re.M))
     assert {"cle_route", "cle_dispatch", "cle_grouped_expert_ffn", "cle_combine",
-            "cle_workload_stats", "cle_schedule_step", "cle_workspace_bytes"} <= declared
+            "cle_workload_stats", "cle_schedule_step", "cle_workspace_bytes",
+            "cle_route_many", "cle_dispatch_many", "cle_combine_many"} <= declared
     for name in declared:
         assert hasattr(cle._lib, name), name
     assert cle.version().count(".") == 2
@@ -41,6 +42,13 @@ def test_workspace_bytes():
     assert b >= 256 + 4 * 128 * 56 and b % 256 == 0
     assert cle.workspace_bytes(cle.OP_FFN, 0, 64, 1, 2, 65) == 0
     assert cle.workspace_bytes(99, 1, 1, 1) == 0
+    # one dispatch workspace per micro-batch of a cle_dispatch_many call
+    one = cle.workspace_bytes(cle.OP_DISPATCH, 2048, 128, 8)
+    assert cle.workspace_bytes(cle.OP_DISPATCH_MANY, 2048, 128, 8, 0, 3) == 3 * one
+    assert cle.workspace_bytes(cle.OP_DISPATCH_MANY, 100, 7, 3, 0, 64) == \
+        64 * cle.workspace_bytes(cle.OP_DISPATCH, 100, 7, 3)
+    assert cle.workspace_bytes(cle.OP_DISPATCH_MANY, 16, 8, 2, 0, 0) == 0
+    assert cle.workspace_bytes(cle.OP_DISPATCH_MANY, 16, 8, 2, 0, 65) == 0
 
 
 def test_invalid_arguments_rejected_on_host():
@@ -66,6 +74,48 @@ def test_invalid_arguments_rejected_on_host():
     d[0].layer = 2
     assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, None, 0,
                                     None, None) == cle.EINVAL              # layer >= L
+
+
+def test_batched_calls_validate_on_host():
+    """The _many entry points reject bad counts, NULL pointer arrays, NULL
+    entries and short workspaces before any HIP call; T == 0 is a no-op."""
+    import ctypes
+    L = cle._lib
+    vp = ctypes.c_void_p
+
+    def arr(*v):
+        return (vp * len(v))(*v)
+
+    one, null1 = arr(16), arr(None)
+    three = arr(16, 32, 48)
+    # route_many(n, logits, T, E, k, idx, gate, stream)
+    assert L.cle_route_many(0, one, 4, 8, 2, one, one, None) == cle.EINVAL     # n < 1
+    assert L.cle_route_many(65, one, 4, 8, 2, one, one, None) == cle.EINVAL    # n > 64
+    assert L.cle_route_many(1, None, 4, 8, 2, one, one, None) == cle.EINVAL    # no array
+    assert L.cle_route_many(1, null1, 4, 8, 2, one, one, None) == cle.EINVAL   # NULL entry
+    assert L.cle_route_many(1, one, 4, 8, 9, one, one, None) == cle.EINVAL     # k > E
+    assert L.cle_route_many(3, three, 0, 8, 2, three, three, None) == cle.OK   # T == 0
+    # dispatch_many(n, idx, T, k, E, counts, offsets, dest, src, ws, ws_bytes, stream)
+    need = cle.workspace_bytes(cle.OP_DISPATCH_MANY, 4, 8, 2, 0, 3)
+    assert L.cle_dispatch_many(3, three, 4, 2, 8, three, three, three, three, 256, need - 1,
+                               None) == cle.EWORKSPACE
+    assert L.cle_dispatch_many(3, three, 4, 2, 8, three, three, three, three, 255, need,
+                               None) == cle.EWORKSPACE                        # unaligned ws
+    assert L.cle_dispatch_many(3, three, 4, 2, 8, three, arr(16, None, 48), three, three, 256,
+                               need, None) == cle.EINVAL                      # NULL offsets entry
+    assert L.cle_dispatch_many(1, one, 4, 2, 2000, one, one, one, one, 256, 1 << 20,
+                               None) == cle.EINVAL                            # E > max
+    # combine_many(n, yp, dest, gate, T, k, H, y_shared, n_shared, residual, y, dt, stream)
+    assert L.cle_combine_many(1, one, one, one, 4, 2, 12, None, 0, None, one, 0,
+                              None) == cle.EINVAL                             # H % 8
+    assert L.cle_combine_many(1, one, one, one, 4, 2, 64, None, 1, None, one, 0,
+                              None) == cle.EINVAL                             # shared, no array
+    assert L.cle_combine_many(1, one, one, one, 4, 2, 64, None, 0, None, arr(8), 0,
+                              None) == cle.EINVAL                             # y not 16-aligned
+    assert L.cle_combine_many(1, one, one, one, 4, 2, 64, None, 0, None, one, 5,
+                              None) == cle.EINVAL                             # dtype
+    assert L.cle_combine_many(2, arr(16, 32), arr(16, 32), arr(16, 32), 0, 2, 64, None, 0,
+                              None, arr(16, 32), 0, None) == cle.OK           # T == 0
 
 
 def test_schedule_step_errors():
