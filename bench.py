@@ -104,6 +104,12 @@ def setup(cfg, seed, dev):
     import synth
     t0 = time.time()
     W = synth.weights_torch(cfg, seed, dev)
+    if cfg.dtype == "bf16":
+        # one-time re-layout for the expert launch (results are bitwise the same)
+        import cross_layer_expert_amd as cle
+        for w in W:
+            if w is not None:
+                cle.pack_weights_inplace(w)
     logits = np.stack([np.stack([synth.logits(cfg, seed, j, l) for l in range(cfg.L)])
                        for j in range(cfg.n)])
     lt = torch.from_numpy(logits).to(dev)
@@ -249,8 +255,9 @@ def main():
 
     W, lt, ht, logits, h0 = setup(cfg, args.seed, dev)
     stream = torch.cuda.current_stream()
+    packed = cfg.dtype == "bf16"
     eng = Engine(W, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
-                 stream=stream)
+                 stream=stream, packed=packed)
     hip = HipEvents()
 
     def one_step(events=None):
@@ -332,7 +339,7 @@ def main():
         runs = {}
         for name, pol, mm in (("b0", cle.POLICY_B0_ALONE, 1), (args.policy, policy, m)):
             e2 = Engine(W, lt, ht, cfg.D, cfg.k, pol, mm, start_layers=cfg.start_layers,
-                        stream=stream)
+                        stream=stream, packed=packed)
             e2.step()
             e2.reset()
             torch.cuda.synchronize()

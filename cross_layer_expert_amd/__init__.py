@@ -22,6 +22,7 @@ BF16, F32 = 0, 1
 POLICY_B0_ALONE, POLICY_B1_LOCKSTEP, POLICY_CUMUTIL, POLICY_MAXUTIL, POLICY_DIFFPEAK = range(5)
 POLICIES = {"b0": 0, "b1": 1, "cumutil": 2, "maxutil": 3, "diffpeak": 4}
 OP_DISPATCH, OP_FFN, OP_DISPATCH_MANY = 1, 2, 3
+W_ROWMAJOR, W_PACKED = 0, 1
 MAX_E, MAX_MICROBATCHES, MAX_MAXUTIL_POOL, MAX_DESC = 1024, 64, 20, 64
 
 
@@ -64,8 +65,9 @@ _sig = {
     "cle_dispatch": (_i32, [_vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                             _vp, _sz, _vp]),
     "cle_grouped_expert_ffn": (_i32, [ctypes.POINTER(FfnDesc), _i32, _vp, _vp, _vp, _vp, _i32,
-                                      _i32, _i32, _i32, _i32, _i32, _vp, _sz,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                       ctypes.POINTER(_vp), _vp]),
+    "cle_pack_weights": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "cle_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp]),
     "cle_workload_stats": (_i32, [_vp, _i32, _i32, _i32, _u64, _vp, _vp, _vp]),
     "cle_schedule_step": (_i32, [ctypes.POINTER(_i32), _i32, _i32, _u64, _i32, _i32,
@@ -179,8 +181,9 @@ def make_desc(layer, rows, offsets, xp, act, yp, shared_rows=0, x_shared=None, a
 
 
 def grouped_expert_ffn(descs, w13, w2, ws, w13_shared=None, w2_shared=None, events=None,
-                       stream=None):
-    """descs: list of FfnDesc.  w13 [L, E, 2I, H], w2 [L, E, H, I].
+                       stream=None, packed=False):
+    """descs: list of FfnDesc.  w13 [L, E, 2I, H], w2 [L, E, H, I] (shapes of the
+    row-major tensors; packed=True when all four were written by pack_weights).
     events: None or 3 raw hipEvent_t handles (ints)."""
     L, E, I2, H = w13.shape
     ns = 0 if w13_shared is None else w13_shared.shape[1]
@@ -190,7 +193,32 @@ def grouped_expert_ffn(descs, w13, w2, ws, w13_shared=None, w2_shared=None, even
         ev = (_vp * 3)(*events)
     _check("cle_grouped_expert_ffn", _lib.cle_grouped_expert_ffn(
         arr, len(descs), _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared), L, E, ns, H,
-        I2 // 2, _dt(w13), _ptr(ws), ws.numel() * ws.element_size(), ev, _stream(stream)))
+        I2 // 2, _dt(w13), W_PACKED if packed else W_ROWMAJOR, _ptr(ws),
+        ws.numel() * ws.element_size(), ev, _stream(stream)))
+
+
+def pack_weights(src, dst=None, stream=None):
+    """Packed copy of a bf16 weight tensor [..., R, K] (the matrices are the
+    last two dimensions); dst: a tensor of the same size, or None for a new one."""
+    import torch
+    if dst is None:
+        dst = torch.empty_like(src)
+    R, K = src.shape[-2], src.shape[-1]
+    n = src.numel() // (R * K)
+    _check("cle_pack_weights", _lib.cle_pack_weights(_ptr(src), _ptr(dst), n, R, K, _dt(src),
+                                                     _stream(stream)))
+    return dst
+
+
+def pack_weights_inplace(t, mats_per_chunk=64, stream=None):
+    """Pack a bf16 weight tensor [..., R, K] in place, through a scratch copy of
+    at most mats_per_chunk matrices at a time (so no second full-size copy)."""
+    R, K = t.shape[-2], t.shape[-1]
+    flat = t.view(-1, R, K)
+    for a in range(0, flat.shape[0], mats_per_chunk):
+        part = flat[a:a + mats_per_chunk]
+        part.copy_(pack_weights(part, stream=stream))
+    return t
 
 
 def combine(yp, dest, topk_gate, y, y_shared=None, residual=None, stream=None):

@@ -270,9 +270,9 @@ struct StageLDS {
 // The stages, referenced by name (one set per kernel instantiation), so the
 // compiler can tell which stage each direct load writes and each read reads,
 // and waits only for the loads a read depends on.
-template <int PHASE, int WN, int NB> __shared__ StageLDS g_st0;
-template <int PHASE, int WN, int NB> __shared__ StageLDS g_st1;
-template <int PHASE, int WN, int NB> __shared__ StageLDS g_st2;
+template <int PHASE, int WN, int NB, bool PACKED> __shared__ StageLDS g_st0;
+template <int PHASE, int WN, int NB, bool PACKED> __shared__ StageLDS g_st1;
+template <int PHASE, int WN, int NB, bool PACKED> __shared__ StageLDS g_st2;
 
 // Everything one tile needs, resolved from the segment table.
 struct TileArgs {
@@ -311,7 +311,7 @@ __device__ __forceinline__ void half_step_order() {
 
 // The K loop and epilogue of one tile computing NMB 16-row blocks (a
 // compile-time count, so the MFMA sequence has no data-dependent branches).
-template <int PHASE, int WN, int NB, int NMB>
+template <int PHASE, int WN, int NB, bool PACKED, int NMB>
 __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) {
   static_assert(WN * NB <= kBlocks, "weight blocks per tile");
   constexpr int XB = kMB / WN;  // A row blocks loaded by each wavefront
@@ -324,7 +324,8 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int g = 0; g < 2; ++g)
-      wp[b][g] = (b < HB ? t.wlo : t.whi) + ((b % HB) * 16 + g * 8 + lr) * t.K + lc * 8;
+      wp[b][g] = (b < HB ? t.wlo : t.whi) + (b % HB) * 16 * t.K +
+                 (PACKED ? g * 512 + lane * 8 : (g * 8 + lr) * t.K + lc * 8);
   const uint16_t* xp[XB][2];
 #pragma unroll
   for (int b = 0; b < XB; ++b)
@@ -355,7 +356,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
     const int ko = kr * kKS;                                                        \
     _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
       _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
-        dma16(wp[b][g] + ko, &ST.w[wave * NB + b][g][0]);                           \
+        dma16(wp[b][g] + (PACKED ? kr * 1024 : ko), &ST.w[wave * NB + b][g][0]);     \
     _Pragma("unroll") for (int b = 0; b < XB; ++b)                                  \
       _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
         dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
@@ -404,9 +405,9 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   }
 
   static_assert(kStages == 3, "the pipeline below is written for 3 buffers");
-  auto& st0 = g_st0<PHASE, WN, NB>;
-  auto& st1 = g_st1<PHASE, WN, NB>;
-  auto& st2 = g_st2<PHASE, WN, NB>;
+  auto& st0 = g_st0<PHASE, WN, NB, PACKED>;
+  auto& st1 = g_st1<PHASE, WN, NB, PACKED>;
+  auto& st2 = g_st2<PHASE, WN, NB, PACKED>;
   CLE_ISSUE(st0, 0);
   CLE_ISSUE(st1, min(1, KT - 1));
   CLE_ISSUE(st2, min(2, KT - 1));
@@ -458,7 +459,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   }
 }
 
-template <int PHASE, int WN, int NB>
+template <int PHASE, int WN, int NB, bool PACKED>
 __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restrict__ segs,
                                                             int nseg,
                                                             const int* __restrict__ totals,
@@ -516,14 +517,14 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     t.whi = W + static_cast<int64_t>(whi) * K;
     const int nmb = (t.nrows + 15) / 16;
     switch (nmb) {
-      case 1: tile_nmb<PHASE, WN, NB, 1>(t, wave, lane); break;
-      case 2: tile_nmb<PHASE, WN, NB, 2>(t, wave, lane); break;
-      case 3: tile_nmb<PHASE, WN, NB, 3>(t, wave, lane); break;
-      case 4: tile_nmb<PHASE, WN, NB, 4>(t, wave, lane); break;
-      case 5: tile_nmb<PHASE, WN, NB, 5>(t, wave, lane); break;
-      case 6: tile_nmb<PHASE, WN, NB, 6>(t, wave, lane); break;
-      case 7: tile_nmb<PHASE, WN, NB, 7>(t, wave, lane); break;
-      default: tile_nmb<PHASE, WN, NB, 8>(t, wave, lane); break;
+      case 1: tile_nmb<PHASE, WN, NB, PACKED, 1>(t, wave, lane); break;
+      case 2: tile_nmb<PHASE, WN, NB, PACKED, 2>(t, wave, lane); break;
+      case 3: tile_nmb<PHASE, WN, NB, PACKED, 3>(t, wave, lane); break;
+      case 4: tile_nmb<PHASE, WN, NB, PACKED, 4>(t, wave, lane); break;
+      case 5: tile_nmb<PHASE, WN, NB, PACKED, 5>(t, wave, lane); break;
+      case 6: tile_nmb<PHASE, WN, NB, PACKED, 6>(t, wave, lane); break;
+      case 7: tile_nmb<PHASE, WN, NB, PACKED, 7>(t, wave, lane); break;
+      default: tile_nmb<PHASE, WN, NB, PACKED, 8>(t, wave, lane); break;
     }
     // every wavefront is done reading the stages before the next tile's
     // first requests overwrite them
@@ -602,12 +603,16 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
                                              const void* w13, const void* w2,
                                              const void* w13_shared, const void* w2_shared,
                                              int32_t L, int32_t E, int32_t n_shared, int32_t H,
-                                             int32_t I, cle_dtype dt, void* ws, size_t ws_bytes,
-                                             void* const* phase_events, void* stream) {
+                                             int32_t I, cle_dtype dt, int32_t w_layout, void* ws,
+                                             size_t ws_bytes, void* const* phase_events,
+                                             void* stream) {
   using namespace cle;
   if (!d || n_desc < 1 || n_desc > CLE_MAX_DESC) return CLE_EINVAL;
   if (!w13 || !w2 || L < 1 || E < 1 || E > CLE_MAX_E || n_shared < 0) return CLE_EINVAL;
   if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
+  if (w_layout != CLE_W_ROWMAJOR && !(w_layout == CLE_W_PACKED && dt == CLE_BF16))
+    return CLE_EINVAL;
+  const bool packed = w_layout == CLE_W_PACKED;
   // bf16: 128-row tiles of 16 weight blocks (8 wavefronts x 2; 128 act
   // columns, 256 output columns) when the shape allows it, else of 8 blocks
   // (4 wavefronts x 2).  f32: 64 x 64 tiles.
@@ -677,13 +682,24 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
   if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[0]), s) != hipSuccess)
     return CLE_EHIP;
   static int occ_b1[64], occ_b2[64], occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64];
+  static int occ_b1p[64], occ_b2p[64], occ_c1p[64], occ_c2p[64];
   if (ub1 > 0) {
     if (wide) {
-      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8, 2>, occ_b1, 512));
-      ffn_gemm_bf16<1, 8, 2><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+      if (packed) {
+        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8, 2, true>, occ_b1p, 512));
+        ffn_gemm_bf16<1, 8, 2, true><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+      } else {
+        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8, 2, false>, occ_b1, 512));
+        ffn_gemm_bf16<1, 8, 2, false><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+      }
     } else if (dt == CLE_BF16) {
-      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4, 2>, occ_c1, 256));
-      ffn_gemm_bf16<1, 4, 2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      if (packed) {
+        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4, 2, true>, occ_c1p, 256));
+        ffn_gemm_bf16<1, 4, 2, true><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      } else {
+        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4, 2, false>, occ_c1, 256));
+        ffn_gemm_bf16<1, 4, 2, false><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      }
     } else {
       const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_f32<1>, occ_f1, 256));
       ffn_gemm_f32<1><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
@@ -693,11 +709,21 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
     return CLE_EHIP;
   if (ub2 > 0) {
     if (wide) {
-      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8, 2>, occ_b2, 512));
-      ffn_gemm_bf16<2, 8, 2><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+      if (packed) {
+        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8, 2, true>, occ_b2p, 512));
+        ffn_gemm_bf16<2, 8, 2, true><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+      } else {
+        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8, 2, false>, occ_b2, 512));
+        ffn_gemm_bf16<2, 8, 2, false><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
+      }
     } else if (dt == CLE_BF16) {
-      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4, 2>, occ_c2, 256));
-      ffn_gemm_bf16<2, 4, 2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      if (packed) {
+        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4, 2, true>, occ_c2p, 256));
+        ffn_gemm_bf16<2, 4, 2, true><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      } else {
+        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4, 2, false>, occ_c2, 256));
+        ffn_gemm_bf16<2, 4, 2, false><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
+      }
     } else {
       const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_f32<2>, occ_f2, 256));
       ffn_gemm_f32<2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);

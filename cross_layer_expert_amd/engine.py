@@ -28,12 +28,14 @@ class Engine:
     """Device-resident state of n micro-batches moving through an L-layer MoE stack.
 
     weights: (w13 [L,E,2I,H], w2 [L,E,H,I], w13_shared | None, w2_shared | None),
+    row-major, or all four packed by pack_weights (then packed=True),
     logits: tensor [n, L, T, E] float32 on the device, h0: tensor [n, T, H].
     """
 
     def __init__(self, weights, logits, h0, D, k, policy, m, start_layers=None, stream=None,
-                 fused_gather=True, batched=True):
+                 fused_gather=True, batched=True, packed=False):
         self.w13, self.w2, self.w13s, self.w2s = weights
+        self.packed = packed  # the weights were written by pack_weights (bf16)
         self.L, self.E, I2, self.H = self.w13.shape
         self.I = I2 // 2
         self.ns = 0 if self.w13s is None else self.w13s.shape[1]
@@ -146,7 +148,7 @@ class Engine:
             d.layer = self.l[j]
             descs.append(d)
         grouped_expert_ffn(descs, self.w13, self.w2, self.ws_ffn, self.w13s, self.w2s,
-                           events=events, stream=s)
+                           events=events, stream=s, packed=self.packed)
         if self.batched:
             combine_many([self.yp[j] for j in R], [self.dest[j] for j in R],
                          [self.gates[j] for j in R], [self.h[j] for j in R],

@@ -57,6 +57,12 @@ typedef enum {
   CLE_POLICY_DIFFPEAK = 4
 } cle_policy;
 
+/* Layout of the expert weight tensors given to cle_grouped_expert_ffn. */
+typedef enum {
+  CLE_W_ROWMAJOR = 0, /* each [rows, K] matrix row-major */
+  CLE_W_PACKED = 1    /* bf16 only: as written by cle_pack_weights */
+} cle_w_layout;
+
 /* Workspace-owning operations, for cle_workspace_bytes(). */
 typedef enum { CLE_OP_DISPATCH = 1, CLE_OP_FFN = 2, CLE_OP_DISPATCH_MANY = 3 } cle_op;
 
@@ -174,6 +180,8 @@ typedef struct {
  *              NULL when n_shared == 0.
  *   bf16: fp32 accumulation; Act and Y rounded to bf16 (nearest even).
  *   f32 : fp32 throughout.
+ *   w_layout   CLE_W_ROWMAJOR, or CLE_W_PACKED (bf16 only) for all four weight
+ *              tensors (see cle_pack_weights).
  *   phase_events: NULL, or HOST array of 3 hipEvent_t recorded on `stream`
  *              after the planning kernel, after the gate/up phase and after
  *              the down phase (for measurement).
@@ -186,8 +194,24 @@ cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_desc,
                                   const void* w13, const void* w2,
                                   const void* w13_shared, const void* w2_shared,
                                   int32_t L, int32_t E, int32_t n_shared, int32_t H, int32_t I,
-                                  cle_dtype dt, void* ws, size_t ws_bytes,
+                                  cle_dtype dt, int32_t w_layout, void* ws, size_t ws_bytes,
                                   void* const* phase_events, void* stream);
+
+/*
+ * cle_pack_weights -- re-lays out n_mat row-major bf16 matrices [R, K] (src)
+ * into the CLE_W_PACKED layout (dst, same size, must not overlap src), for
+ * cle_grouped_expert_ffn with w_layout = CLE_W_PACKED.  Pack each of w13
+ * ([L*E] matrices of [2I, H]), w2 ([L*E] of [H, I]) and the shared-expert
+ * tensors once, when the weights are loaded.
+ * Layout: blocks of 16 rows x 64 K (2 KiB) in (row block, K block) order; a
+ * block holds two 1 KiB groups (rows 0-7, rows 8-15); in a group, the 16-byte
+ * chunk c (K elements 8c .. 8c+7 of the block) of row r is at position
+ * r * 8 + (c ^ r).  Results of the expert launch are bitwise the same for
+ * both layouts.
+ * Requires dt == CLE_BF16, R % 16 == 0, K % 64 == 0, 16-byte aligned pointers.
+ */
+cle_status cle_pack_weights(const void* src, void* dst, int64_t n_mat, int32_t R, int32_t K,
+                            cle_dtype dt, void* stream);
 
 /*
  * cle_combine -- gate-weighted sum of each token's expert outputs (paper

@@ -65,14 +65,23 @@ def test_invalid_arguments_rejected_on_host():
     assert L.cle_workload_stats(8, 2, 8, 3, 0, 8, None, None) == cle.EINVAL  # E % D
     assert L.cle_workload_stats(8, 2, 8, 4, 0b100, 8, 8, None) == cle.EINVAL  # mask bit >= n
     d = (cle.FfnDesc * 1)(cle.FfnDesc(0, 8, 16, 16, 16, 16, 0, None, None, None))
-    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 96, 64, 1, None, 0,
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 96, 64, 1, 0, None, 0,
                                     None, None) == cle.EINVAL              # f32: H % 64
-    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 64, 64, 0, None, 0,
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 64, 64, 0, 0, None, 0,
                                     None, None) == cle.EINVAL              # bf16: H % 128
-    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, None, 0,
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, 0, None, 0,
                                     None, None) == cle.EWORKSPACE
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 1, 1, None, 0,
+                                    None, None) == cle.EINVAL              # packed needs bf16
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, 2, None, 0,
+                                    None, None) == cle.EINVAL              # unknown layout
+    assert L.cle_pack_weights(16, 4096, 1, 24, 64, 0, None) == cle.EINVAL  # R % 16
+    assert L.cle_pack_weights(16, 4096, 1, 16, 96, 0, None) == cle.EINVAL  # K % 64
+    assert L.cle_pack_weights(16, 4096, 1, 16, 64, 1, None) == cle.EINVAL  # f32
+    assert L.cle_pack_weights(16, 1024, 1, 16, 64, 0, None) == cle.EINVAL  # overlapping
+    assert L.cle_pack_weights(None, None, 0, 16, 64, 0, None) == cle.OK    # nothing to pack
     d[0].layer = 2
-    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, None, 0,
+    assert L.cle_grouped_expert_ffn(d, 1, 16, 16, None, None, 2, 8, 0, 128, 64, 0, 0, None, 0,
                                     None, None) == cle.EINVAL              # layer >= L
 
 
