@@ -3,23 +3,31 @@
 A timed step is one iteration of Algorithm 1 of EasyBalance over the
 Qwen3-30B-A3B-shaped synthetic stack (48 layers, hidden 2048, 128 experts
 top-8, SwiGLU intermediate 768, D = 8 groups, 4 micro-batches of 2048
-tokens): route + dispatch of the previous RunSet, workload statistics, the
-host scheduler (CumUtil, m = 3), one grouped expert launch per GEMM phase for
-every RunSet member at its own layer, and the gate-weighted combine.  When all
-micro-batches have passed layer 48 the engine restarts at layer 0.
+tokens): route + dispatch of the previous RunSet, the workload statistics
+and Schedule(S, m) (CumUtil, m = 3), one grouped expert launch per GEMM phase
+for every RunSet member at its own layer, and the gate-weighted combine.  By
+default the step is one cle_loop_step (the schedule runs on the device and the
+host never waits); --host-loop times the host-driven step instead (workloads
+copied to the host, the host scheduler, then the launches).  When all
+micro-batches have passed layer 48 the loop restarts at layer 0 from the
+initial hidden states.
 
 Prints one JSON line (rank 0):
   value      expert tokens/s over the timed steps (inputs resident in HBM);
   roofline   the dominant kernel (grouped gate/up GEMM): algorithmic bytes or
-             FLOPs per launch / its mean launch time from HIP events recorded
-             on the library's stream during the timed steps;
-  cpu_baseline the CPU oracle on one (micro-batch, layer) unit of the same
-             workload, on this host's cores.
+             FLOPs per launch / its mean launch time, from start/end HIP
+             events that the launch itself records on the library's stream
+             during the timed steps;
+  cpu_baseline the CPU oracle on (micro-batch, layer) units of the same
+             workload, on this host's cores (and on one core).
+With --sweep it prints instead the 1-u sweep over n, m/n and D and the
+consecutive-layer same-peak counts, one JSON line per (config, D).
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import gc
 import hashlib
 import json
 import os
@@ -69,6 +77,10 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, e, stream_handle):
+        assert self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream_handle)) == 0
 
     def create(self, n):
         out = []
@@ -104,12 +116,6 @@ def setup(cfg, seed, dev):
     import synth
     t0 = time.time()
     W = synth.weights_torch(cfg, seed, dev)
-    if cfg.dtype == "bf16":
-        # one-time re-layout for the expert launch (results are bitwise the same)
-        import cross_layer_expert_amd as cle
-        for w in W:
-            if w is not None:
-                cle.pack_weights_inplace(w)
     logits = np.stack([np.stack([synth.logits(cfg, seed, j, l) for l in range(cfg.L)])
                        for j in range(cfg.n)])
     lt = torch.from_numpy(logits).to(dev)
@@ -154,16 +160,17 @@ def ffn_work(cfg, members, counts_host):
     return b1, b2, f1, f2
 
 
-def schedule_only_u(cfg, w_table, policy, m):
+def schedule_only_u(w_table, D, policy, m, start_layers=None):
     """1-u of Algorithm 1 over a full run, from the per-(micro-batch, layer)
-    workloads, with the library's host scheduler."""
+    workloads w_table[j][l] (length D), with the library's host scheduler.
+    Returns (1-u, steps, sum of members' own peaks / sum of step peaks)."""
     import cross_layer_expert_amd as cle
-    n, L = cfg.n, cfg.L
-    lj = list(cfg.start_layers) if cfg.start_layers else [0] * n
+    n, L = len(w_table), len(w_table[0])
+    lj = list(start_layers) if start_layers else [0] * n
     S = [j for j in range(n) if lj[j] < L]
     num = den = sep = steps = 0
     while S:
-        w = np.zeros((n, cfg.D), np.int32)
+        w = np.zeros((n, D), np.int32)
         for j in S:
             w[j] = w_table[j][lj[j]]
         R = cle.ids_of(cle.schedule_step(w, cle.mask_of(S), m, policy))
@@ -175,38 +182,132 @@ def schedule_only_u(cfg, w_table, policy, m):
         for j in R:
             lj[j] += 1
         S = [j for j in S if lj[j] < L]
-    return 1.0 - num / (cfg.D * den), steps, sep / den
+    return 1.0 - num / (D * den), steps, sep / den
 
 
-def cpu_baseline(cfg, W, logits, h0, budget_s):
-    """The CPU oracle on (micro-batch, layer) units of the same workload."""
+def same_peak(w_table, run):
+    """Windows of `run` consecutive layers whose peak group (lowest index among
+    equal maxima) is the same on every layer, summed over micro-batches
+    (the statistic of the EasyBalance paper's Table 2): (hits, windows)."""
+    hits = windows = 0
+    for wj in w_table:
+        peaks = np.argmax(np.asarray(wj), axis=1)      # first maximum = lowest index
+        nwin = max(0, len(peaks) - run + 1)
+        if nwin:
+            same = np.ones(nwin, bool)
+            for q in range(1, run):
+                same &= peaks[q:q + nwin] == peaks[:nwin]
+            hits += int(same.sum())
+        windows += nwin
+    return hits, windows
+
+
+def workload_tables(cfg, seed, dev, n, Ds):
+    """{D: int array [n, L, D]}: per-(micro-batch, layer) group workloads from
+    the library's route, dispatch and workload-statistics kernels (one batched
+    call per micro-batch covers all L layers)."""
+    import torch
+    import cross_layer_expert_amd as cle
+    import synth
+    L, T, E, k = cfg.L, cfg.T, cfg.E, cfg.k
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx = torch.empty((L, T, k), **i32)
+    gate = torch.empty((L, T, k), dtype=torch.float32, device=dev)
+    counts, offsets = torch.empty((L, E), **i32), torch.empty((L, E + 1), **i32)
+    dest, src = torch.empty((L, T * k), **i32), torch.empty((L, T * k), **i32)
+    ws = torch.empty(cle.workspace_bytes(cle.OP_DISPATCH_MANY, T, E, k, 0, L) // 4, **i32)
+    out = {D: np.zeros((n, L, D), np.int64) for D in Ds}
+    for j in range(n):
+        lg = torch.from_numpy(np.stack([synth.logits(cfg, seed, j, l) for l in range(L)])).to(dev)
+        cle.route_many(list(lg), k, list(idx), list(gate))
+        cle.dispatch_many(list(idx), E, list(counts), list(offsets), list(dest), list(src), ws)
+        for D in Ds:
+            wd = torch.empty((L, D), **i32)
+            cle.workload_stats(counts, D, 0, wd)
+            out[D][j] = wd.cpu().numpy()
+    return out
+
+
+SWEEP_POLICIES = ("b0", "b1", "cumutil", "maxutil", "diffpeak")
+
+
+def sweep(seed, dev, configs=("qwen3", "moonlight", "taskshift"), ns=(2, 4, 8, 16),
+          ratios=(0.5, 0.75, 1.0), Ds=(2, 4, 8)):
+    """1-u of every policy over n, m/n and D, and the consecutive-layer
+    same-peak rates; one JSON line per (config, D)."""
+    import cross_layer_expert_amd as cle
+    import synth
+    for name in configs:
+        cfg = synth.CONFIGS[name]
+        t0 = time.time()
+        tables = workload_tables(cfg, seed, dev, max(ns), Ds)
+        for D in Ds:
+            wt = tables[D]
+            line = {"sweep": name, "seed": seed, "D": D, "L": cfg.L, "T": cfg.T, "E": cfg.E,
+                    "k": cfg.k, "zipf_s": cfg.zipf_s, "profiles": cfg.profiles}
+            sp = {}
+            for run in (2, 3):
+                h, w = same_peak(wt[:max(ns)], run)
+                sp[str(run)] = [h, w, round(h / w, 4) if w else None]
+            line["same_peak"] = sp
+            pts = []
+            for n in ns:
+                base = {}
+                for pol in ("b0", "b1"):
+                    om, st, _ = schedule_only_u(wt[:n], D, cle.POLICIES[pol], 1)
+                    base[pol] = (round(om, 4), st)
+                for r in ratios:
+                    m = max(1, int(r * n))
+                    pt = {"n": n, "m": m, "one_minus_u": {}, "steps": {}}
+                    for pol in SWEEP_POLICIES:
+                        if pol in base:
+                            om, st = base[pol]
+                        else:
+                            om, st, _ = schedule_only_u(wt[:n], D, cle.POLICIES[pol], m)
+                            om = round(om, 4)
+                        pt["one_minus_u"][pol] = om
+                        pt["steps"][pol] = st
+                    pts.append(pt)
+            line["points"] = pts
+            line["seconds"] = round(time.time() - t0, 1)
+            print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None):
+    """The CPU oracle on (micro-batch, layer) units of the same workload:
+    route, dispatch, float64 SwiGLU experts (numpy matmul) and the combine of
+    micro-batch 0 at layers 0, 1, ... until budget_s of oracle time is spent.
+    threads: BLAS threads (None = every core this process may run on)."""
+    import torch
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    done_tok, spent, units = 0, 0.0, []
-    j = 0
-    for l in range(cfg.L):
-        w13 = oracle.widen(W[0][l].cpu().view(__import__("torch").int16).numpy().view(np.uint16),
-                           "bf16")
-        w2 = oracle.widen(W[1][l].cpu().view(__import__("torch").int16).numpy().view(np.uint16),
-                          "bf16")
-        x = oracle.widen(h0[j], "bf16")
-        t0 = time.perf_counter()
-        out = oracle.moe_layer(x, logits[j, l], cfg.k, w13, w2)
-        dt = time.perf_counter() - t0
-        assert np.isfinite(out["y"]).all()
-        spent += dt
-        done_tok += cfg.T * cfg.k
-        units.append((j, l))
-        del w13, w2
-        if spent >= budget_s:
-            break
-    return dict(value=done_tok / spent, unit="expert tokens/s", cores=int(threads), kind="oracle",
-                sample=f"{len(units)} (micro-batch, layer) unit(s) of the {cfg.name} workload "
-                       f"(micro-batch 0, layers 0..{len(units) - 1}; {done_tok} expert tokens; "
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=threads if threads else cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        done_tok, spent, units = 0, 0.0, 0
+        j = 0
+        for l in range(cfg.L):
+            w13 = oracle.widen(W[0][l].cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
+            w2 = oracle.widen(W[1][l].cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
+            ws = [None, None]
+            if W[2] is not None:
+                ws = [oracle.widen(W[q][l].cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
+                      for q in (2, 3)]
+            x = oracle.widen(h0[j], "bf16")
+            t0 = time.perf_counter()
+            out = oracle.moe_layer(x, logits[j, l], cfg.k, w13, w2, ws[0], ws[1])
+            dt = time.perf_counter() - t0
+            assert np.isfinite(out["y"]).all()
+            spent += dt
+            done_tok += cfg.T * (cfg.k + cfg.n_shared)
+            units += 1
+            del w13, w2, ws
+            if spent >= budget_s:
+                break
+    return dict(value=round(done_tok / spent, 1), unit="expert tokens/s", cores=int(used),
+                kind="oracle",
+                sample=f"{units} (micro-batch, layer) unit(s) of the {cfg.name} workload "
+                       f"(micro-batch 0, layers 0..{units - 1}; {done_tok} expert tokens; "
                        f"route, dispatch, float64 SwiGLU experts, combine); {spent:.1f} s")
 
 
@@ -222,6 +323,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip whole-run and 1-u passes")
+    ap.add_argument("--host-loop", action="store_true",
+                    help="time the host-driven step (schedule on the host after a wait for the "
+                         "workloads) instead of the device-driven one")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print the 1-u sweep over n, m/n and D (one JSON line per config and D) "
+                         "instead of the timed step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -238,6 +345,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.sweep:
+        sweep(args.seed, dev)
+        return
     cfg = synth.CONFIGS[args.config]
     m = args.m if args.m is not None else cfg.m
     policy = cle.POLICIES[args.policy]
@@ -255,36 +365,88 @@ def main():
 
     W, lt, ht, logits, h0 = setup(cfg, args.seed, dev)
     stream = torch.cuda.current_stream()
+    # bf16: the expert launch reads a packed copy of the weights (a one-time
+    # re-layout; results are bitwise those of the row-major weights, which the
+    # CPU oracle keeps using)
     packed = cfg.dtype == "bf16"
-    eng = Engine(W, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
-                 stream=stream, packed=packed)
+    Wk = tuple(None if w is None else cle.pack_weights(w) for w in W) if packed else W
+    torch.cuda.synchronize()
+    K, Wm = args.steps, args.warmup
+    C = min(K, 40)
+    device_loop = not args.host_loop
+    # device loop: every step is one cle_loop_step (schedule on the device, no
+    # host wait); when all micro-batches finish, the loop restarts from h0
+    # inside that step
+    eng = Engine(Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
+                 stream=stream, packed=packed, device_loop=device_loop, restart=device_loop,
+                 log_cap=max(4096, Wm + K + 64))
     hip = HipEvents()
 
-    def one_step(events=None):
-        if eng.done:
-            eng.reset()
-        return eng.step(events=events)
+    def one_step(e, events=None):
+        if not e.device_loop and e.done:
+            e.reset()
+        return e.step(events=events)
 
-    for _ in range(args.warmup):
-        one_step()
+    for _ in range(Wm):
+        one_step(eng)
     torch.cuda.synchronize()
 
-    K = args.steps
-    evs = [hip.create(3) for _ in range(K)]
+    # the expert launches take their own start/end events (no marker between
+    # kernels); Python's cyclic collector stays off while the steps run
+    evs = [hip.create(4) for _ in range(K)]
     steps = []
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        one_step(events=evs[i])
-        R, layers = eng.trace[-1]
-        steps.append(list(zip(R, layers)))
+        one_step(eng, events=evs[i])
+        if not device_loop:
+            R, layers = eng.trace[-1]
+            steps.append(list(zip(R, layers)))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gc.enable()
+    if device_loop:
+        eng.sync_trace()
+        steps = [list(zip(R, layers)) for R, layers in eng.trace[-K:]]
+        assert len(eng.trace) == Wm + K
+
+    # host-driven steps (host schedule after a wait for the workloads) on the
+    # same buffers: a timed pass for comparison, then a pass with markers
+    # around route + dispatch and after the combine (markers cost a few us of
+    # stream time each, so they stay out of the timed steps above)
+    hst = eng if not device_loop else Engine(
+        Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers, stream=stream,
+        packed=packed)
+    for _ in range(5):
+        one_step(hst)
+    torch.cuda.synchronize()
+    HK = min(K, 100)
+    gc.collect()
+    gc.disable()
+    h0t = time.perf_counter()
+    for _ in range(HK):
+        one_step(hst)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - h0t) / HK * 1e3
+    gc.enable()
+    cev = [hip.create(4) for _ in range(C)]
+    marks = [hip.create(3) for _ in range(C)]
+    sh = stream.cuda_stream
+    routed, csteps = [], []
+    for i in range(C):
+        if hst.done:
+            hst.reset()
+        routed.append([(j, hst.l[j]) for j in hst.prev if hst.l[j] < hst.L])
+        hst.step(events=cev[i], mark=lambda q, i=i: hip.record(marks[i][q], sh))
+        csteps.append(hst.trace[-1][0])
+    torch.cuda.synchronize()
 
     tok = sum(len(R) * cfg.T * (cfg.k + cfg.n_shared) for R in steps)
     value = tok / elapsed
     g1 = [hip.ms(e[0], e[1]) for e in evs]
-    g2 = [hip.ms(e[1], e[2]) for e in evs]
+    g2 = [hip.ms(e[2], e[3]) for e in evs]
 
     # algorithmic work of every timed launch (counts recomputed by the library)
     need = sorted({jl for R in steps for jl in R})
@@ -313,12 +475,41 @@ def main():
                 algorithmic_bytes_per_launch=int(B1 / K), flops_per_launch=int(F1 / K))
 
     gemm_tflops = (F1 + F2) / (t1 + t2) / 1e12
+
+    def binding(F, B, t):
+        """Fraction of the binding roofline: max(FLOP / peak, bytes / HBM) / t."""
+        return max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / t
+
+    # route + dispatch of the previous RunSet, and the combine, from events on
+    # the same stream (stream time between the events)
+    esz = 2 if cfg.dtype == "bf16" else 4
+    T, k, H, E, ns = cfg.T, cfg.k, cfg.H, cfg.E, cfg.n_shared
+    rd_unit = T * E * 4 + T * k * 8 + T * k * 4 + T * k * 8 + 2 * E * 4
+    cb_unit = T * k * H * esz + T * k * 8 + (1 + ns) * T * H * esz + T * H * esz
+    rd_ms = [hip.ms(mk[0], mk[1]) for mk, r in zip(marks, routed) if r]
+    rd_bytes = sum(len(r) for r in routed) * rd_unit
+    cb_ms = [hip.ms(e[3], mk[2]) for e, mk in zip(cev, marks)]
+    cb_bytes = sum(len(R) for R in csteps) * cb_unit
+    t_rd, t_cb = sum(rd_ms) / 1e3, sum(cb_ms) / 1e3
     extras = dict(
         gemm_tflops=round(gemm_tflops, 1),
         mfma_peak_frac=round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
-        gemm_hbm_frac=round((B1 + B2) / (t1 + t2) / 1e9 / HBM_PEAK_GBS, 4),
-        down_mean_launch_us=round(t2 / K * 1e6, 2),
+        gemm_hbm_gbs=round((B1 + B2) / (t1 + t2) / 1e9, 1),
+        gemm_binding_roofline_frac=round(binding(F1 + F2, B1 + B2, t1 + t2), 4),
+        gate_up=dict(mean_us=round(t1 / K * 1e6, 2), median_us=round(float(np.median(g1)) * 1e3, 2),
+                     tflops=round(F1 / t1 / 1e12, 1), gbs=round(B1 / t1 / 1e9, 1),
+                     binding_roofline_frac=round(binding(F1, B1, t1), 4)),
+        down=dict(mean_us=round(t2 / K * 1e6, 2), median_us=round(float(np.median(g2)) * 1e3, 2),
+                  tflops=round(F2 / t2 / 1e12, 1), gbs=round(B2 / t2 / 1e9, 1),
+                  binding_roofline_frac=round(binding(F2, B2, t2), 4)),
+        route_dispatch=dict(mean_us=round(t_rd / max(len(rd_ms), 1) * 1e6, 2),
+                            gbs=round(rd_bytes / t_rd / 1e9, 1) if t_rd else None,
+                            bytes_per_microbatch=rd_unit),
+        combine=dict(mean_us=round(t_cb / C * 1e6, 2), gbs=round(cb_bytes / t_cb / 1e9, 1),
+                     bytes_per_microbatch=cb_unit),
         ffn_share_of_step=round((t1 + t2) / elapsed, 3),
+        loop="device" if device_loop else "host",
+        host_loop_ms_per_step=round(host_ms, 4),
     )
 
     if not args.no_extras:
@@ -331,29 +522,33 @@ def main():
                 cle.workload_stats(c, cfg.D, 0, wd)
                 w_table[j][l] = wd.cpu().numpy()[0]
         uu = {}
-        for name in ("b0", "b1", "cumutil", "maxutil", "diffpeak"):
-            one_minus_u, nsteps, ratio = schedule_only_u(cfg, w_table, cle.POLICIES[name], m)
+        for name in SWEEP_POLICIES:
+            one_minus_u, nsteps, ratio = schedule_only_u(w_table, cfg.D, cle.POLICIES[name], m,
+                                                         cfg.start_layers)
             uu[name] = dict(one_minus_u=round(one_minus_u, 4), steps=nsteps)
         extras["under_util"] = uu
         # measured whole runs: cross-layer (timed policy) vs one (j, l) per step
         runs = {}
         for name, pol, mm in (("b0", cle.POLICY_B0_ALONE, 1), (args.policy, policy, m)):
-            e2 = Engine(W, lt, ht, cfg.D, cfg.k, pol, mm, start_layers=cfg.start_layers,
-                        stream=stream, packed=packed)
-            e2.step()
-            e2.reset()
-            torch.cuda.synchronize()
-            s0 = time.perf_counter()
-            e2.run()
-            torch.cuda.synchronize()
-            runs[name] = dict(ms=round((time.perf_counter() - s0) * 1e3, 2),
-                              steps=len(e2.trace), one_minus_u=round(1 - e2.stats()[1], 4))
-            del e2
+            for dl in (False, True):
+                e2 = Engine(Wk, lt, ht, cfg.D, cfg.k, pol, mm, start_layers=cfg.start_layers,
+                            stream=stream, packed=packed, device_loop=dl)
+                e2.step()
+                e2.reset()
+                torch.cuda.synchronize()
+                s0 = time.perf_counter()
+                e2.run(chunk=max(1, cfg.L // 2)) if dl else e2.run()
+                torch.cuda.synchronize()
+                runs[name + ("_device" if dl else "_host")] = dict(
+                    ms=round((time.perf_counter() - s0) * 1e3, 2), steps=len(e2.trace),
+                    one_minus_u=round(1 - e2.stats()[1], 4))
+                del e2
         extras["whole_run"] = runs
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, W, logits, h0, args.cpu_budget)
+        cpu["one_core"] = cpu_baseline(cfg, W, logits, h0, args.cpu_budget / 2, threads=1)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "expert tokens/s", "n_gpus": 1,
@@ -361,6 +556,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded router logits with Zipf skew, N(0,1) hidden, N(0,0.02) weights)",
         "config": {"workload": workload_name(cfg), "policy": args.policy if policy != 1 else "b1",
+                   "schedule": "device" if device_loop else "host",
                    "m": m, "seed": args.seed, "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu,
     }

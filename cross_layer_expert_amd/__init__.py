@@ -55,7 +55,34 @@ class FfnDesc(ctypes.Structure):
                 ("y_shared", _vp), ("x", _vp), ("src", _vp), ("k", _i32)]
 
 
+_P64 = _vp * 64
+
+
+class LoopState(ctypes.Structure):
+    """Mirror of ``cle_loop_state`` (read back from device memory)."""
+    _fields_ = [("layer", _i32 * 64), ("run_layer", _i32 * 64), ("start", _i32 * 64),
+                ("ready", _u64), ("todo", _u64), ("runset", _u64), ("acc", _i64 * 4),
+                ("n", _i32), ("L", _i32), ("restarts", _i32), ("restarted", _i32)]
+
+
+class LoopDesc(ctypes.Structure):
+    """Mirror of ``cle_loop_desc``."""
+    _fields_ = [(f, _i32) for f in ("n", "L", "T", "E", "k", "H", "I", "D", "m", "policy",
+                                    "n_shared", "dtype", "w_layout", "restart")] + \
+               [(f, _P64) for f in ("logits", "h", "h0", "idx", "gate", "counts", "offsets",
+                                    "dest", "src", "act", "yp", "act_shared", "y_shared")] + \
+               [("w13", _vp), ("w2", _vp), ("w13_shared", _vp), ("w2_shared", _vp),
+                ("ws_dispatch", _vp), ("ws_dispatch_bytes", _sz), ("ws_ffn", _vp),
+                ("ws_ffn_bytes", _sz), ("w", _vp), ("log", _vp), ("log_cap", _i64),
+                ("state", _vp)]
+
+
+LOOP_STATE_BYTES = ctypes.sizeof(LoopState)
+
 _sig = {
+    "cle_schedule_step_device": (_i32, [_vp, _i32, _i32, _u64, _i32, _i32, _vp, _vp]),
+    "cle_loop_init": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_i32), _vp]),
+    "cle_loop_step": (_i32, [ctypes.POINTER(LoopDesc), ctypes.POINTER(_vp), _vp]),
     "cle_route": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "cle_route_many": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "cle_dispatch_many": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -184,13 +211,16 @@ def grouped_expert_ffn(descs, w13, w2, ws, w13_shared=None, w2_shared=None, even
                        stream=None, packed=False):
     """descs: list of FfnDesc.  w13 [L, E, 2I, H], w2 [L, E, H, I] (shapes of the
     row-major tensors; packed=True when all four were written by pack_weights).
-    events: None or 3 raw hipEvent_t handles (ints)."""
+    events: None or 4 raw hipEvent_t handles (ints): start and end of the
+    gate/up kernel, then of the down kernel."""
     L, E, I2, H = w13.shape
     ns = 0 if w13_shared is None else w13_shared.shape[1]
     arr = (FfnDesc * len(descs))(*descs)
     ev = None
     if events is not None:
-        ev = (_vp * 3)(*events)
+        if len(events) != 4:
+            raise ValueError("events: 4 hipEvent_t handles")
+        ev = (_vp * 4)(*events)
     _check("cle_grouped_expert_ffn", _lib.cle_grouped_expert_ffn(
         arr, len(descs), _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared), L, E, ns, H,
         I2 // 2, _dt(w13), W_PACKED if packed else W_ROWMAJOR, _ptr(ws),
@@ -265,3 +295,35 @@ def mask_of(ids) -> int:
 
 def ids_of(mask: int) -> list:
     return [j for j in range(64) if mask >> j & 1]
+
+
+# ---------------------------------------------------------------- device-driven loop
+def schedule_step_device(w, ready_mask, m, policy, runset, stream=None):
+    """w: device int32 [n, D]; runset: device tensor of >= 8 bytes (uint64 out)."""
+    n, D = w.shape
+    _check("cle_schedule_step_device", _lib.cle_schedule_step_device(
+        _ptr(w), n, D, int(ready_mask), m, int(policy), _ptr(runset), _stream(stream)))
+
+
+def loop_init(state, n, L, start=None, stream=None):
+    """state: device tensor of >= LOOP_STATE_BYTES bytes (8-byte aligned)."""
+    st = None
+    if start is not None:
+        st = (_i32 * n)(*[int(v) for v in start])
+    _check("cle_loop_init", _lib.cle_loop_init(_ptr(state), n, L, st, _stream(stream)))
+
+
+def loop_step(desc, events=None, stream=None):
+    """desc: a LoopDesc; events: None or 4 hipEvent_t handles (see grouped_expert_ffn)."""
+    ev = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events: 4 hipEvent_t handles")
+        ev = (_vp * 4)(*events)
+    _check("cle_loop_step", _lib.cle_loop_step(ctypes.byref(desc), ev, _stream(stream)))
+
+
+def read_loop_state(state) -> LoopState:
+    """Copy the state back (synchronises the current stream with the copy)."""
+    raw = state.view(__import__("torch").uint8)[:LOOP_STATE_BYTES].cpu().numpy()
+    return LoopState.from_buffer_copy(raw.tobytes())

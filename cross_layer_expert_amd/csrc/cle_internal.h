@@ -20,6 +20,30 @@ inline cle_status launch_status() {
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Launchers behind the batched entry points, for callers that validated
+// their arguments already.  `st` (may be NULL) restricts a launch to the
+// micro-batches of the loop state's todo (route, dispatch) or runset
+// (combine, expert FFN) mask; the kernels read the mask on the device.
+cle_status launch_route(int n, const float* const* logits, int T, int E, int k, int* const* idx,
+                        float* const* gate, const cle_loop_state* st, int64_t layer_stride,
+                        hipStream_t s);
+cle_status launch_dispatch_many(int n, const int* const* idx, int T, int k, int E,
+                                int* const* counts, int* const* offsets, int* const* dest,
+                                int* const* src, void* ws, const cle_loop_state* st,
+                                hipStream_t s);
+cle_status launch_combine_many(int n, const void* const* yp, const int* const* dest,
+                               const float* const* gate, int T, int k, int H,
+                               const void* const* y_shared, int n_shared,
+                               const void* const* residual, void* const* y, cle_dtype dt,
+                               const cle_loop_state* st, hipStream_t s);
+// cle_grouped_expert_ffn with an optional loop state; launch = false only
+// validates the arguments.
+cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, const void* w2,
+                       const void* w13_shared, const void* w2_shared, int32_t L, int32_t E,
+                       int32_t n_shared, int32_t H, int32_t I, cle_dtype dt, int32_t w_layout,
+                       void* ws, size_t ws_bytes, void* const* phase_events,
+                       const cle_loop_state* st, bool launch, void* stream);
+
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // ---------------------------------------------------------------- bf16

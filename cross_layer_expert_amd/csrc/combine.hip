@@ -57,6 +57,7 @@ struct CombineArgs {
   const void* y_shared[CLE_MAX_MICROBATCHES];
   const void* residual[CLE_MAX_MICROBATCHES];
   void* y[CLE_MAX_MICROBATCHES];
+  const cle_loop_state* st;  // non-NULL: only the members of st->runset
 };
 
 // KMAX > 0: k <= KMAX slots, whose destinations and gates are held in
@@ -66,6 +67,7 @@ struct CombineArgs {
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs args, int T_, int k, int H,
                                                       int n_shared) {
+  if (args.st && !(args.st->runset >> blockIdx.y & 1)) return;  // uniform over the block
   const T* __restrict__ yp = static_cast<const T*>(args.yp[blockIdx.y]);
   const int* __restrict__ dest = args.dest[blockIdx.y];
   const float* __restrict__ gate = args.gate[blockIdx.y];
@@ -162,7 +164,6 @@ extern "C" cle_status cle_combine_many(int32_t n, const void* const* yp,
   if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
   if (T == 0) return CLE_OK;
   if (n_shared > 0 && !y_shared) return CLE_EINVAL;
-  CombineArgs a;
   for (int j = 0; j < n; ++j) {
     const void* ys = y_shared ? y_shared[j] : nullptr;
     const void* res = residual ? residual[j] : nullptr;
@@ -171,17 +172,33 @@ extern "C" cle_status cle_combine_many(int32_t n, const void* const* yp,
     if (!aligned(yp[j], 16) || !aligned(y[j], 16) || (ys && !aligned(ys, 16)) ||
         (res && !aligned(res, 16)))
       return CLE_EINVAL;
+  }
+  return launch_combine_many(n, yp, dest, topk_gate, T, k, H, y_shared, n_shared, residual, y, dt,
+                             nullptr, as_stream(stream));
+}
+
+namespace cle {
+
+cle_status launch_combine_many(int n, const void* const* yp, const int* const* dest,
+                               const float* const* gate, int T, int k, int H,
+                               const void* const* y_shared, int n_shared,
+                               const void* const* residual, void* const* y, cle_dtype dt,
+                               const cle_loop_state* st, hipStream_t s) {
+  CombineArgs a;
+  for (int j = 0; j < n; ++j) {
     a.yp[j] = yp[j];
     a.dest[j] = dest[j];
-    a.gate[j] = topk_gate[j];
-    a.y_shared[j] = ys;
-    a.residual[j] = res;
+    a.gate[j] = gate[j];
+    a.y_shared[j] = y_shared ? y_shared[j] : nullptr;
+    a.residual[j] = residual ? residual[j] : nullptr;
     a.y[j] = y[j];
   }
-  hipStream_t s = as_stream(stream);
+  a.st = st;
   if (dt == CLE_BF16)
     launch_combine<uint16_t>(a, n, T, k, H, n_shared, s);
   else
     launch_combine<float>(a, n, T, k, H, n_shared, s);
   return launch_status();
 }
+
+}  // namespace cle

@@ -32,9 +32,15 @@ struct DispatchArgs {
   int* src[CLE_MAX_MICROBATCHES];
   int* hist;
   int64_t hist_stride;
+  const cle_loop_state* st;  // non-NULL: only micro-batches in st->todo
 };
 
+__device__ __forceinline__ bool skip(const DispatchArgs& a, int j) {
+  return a.st && !(a.st->todo >> j & 1);
+}
+
 __global__ __launch_bounds__(256) void dispatch_count(DispatchArgs args, int64_t A, int E) {
+  if (skip(args, blockIdx.y)) return;
   const int* __restrict__ idx = args.idx[blockIdx.y];
   int* __restrict__ chunk_hist = args.hist + blockIdx.y * args.hist_stride;
   __shared__ int hist[CLE_MAX_E];
@@ -57,6 +63,7 @@ __global__ __launch_bounds__(256) void dispatch_count(DispatchArgs args, int64_t
 // and offsets.
 __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs args, int64_t chunks, int E,
                                                       int64_t A) {
+  if (skip(args, blockIdx.x)) return;
   int* __restrict__ chunk_hist = args.hist + blockIdx.x * args.hist_stride;
   int* __restrict__ counts = args.counts[blockIdx.x];
   int* __restrict__ offsets = args.offsets[blockIdx.x];
@@ -102,6 +109,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs args, int64_t
 
 __global__ __launch_bounds__(256) void dispatch_scatter(DispatchArgs args, int64_t A, int E,
                                                         int id_bits) {
+  if (skip(args, blockIdx.y)) return;
   const int* __restrict__ idx = args.idx[blockIdx.y];
   const int* __restrict__ chunk_base = args.hist + blockIdx.y * args.hist_stride;
   int* __restrict__ dest = args.dest[blockIdx.y];
@@ -238,6 +246,7 @@ extern "C" cle_status cle_dispatch(const int32_t* topk_idx, int32_t T, int32_t k
   a.src[0] = src;
   a.hist = static_cast<int*>(ws);
   a.hist_stride = 0;
+  a.st = nullptr;
   const cle_status st = launch_dispatch(a, 1, A, E, s);
   if (st != CLE_OK || A == 0 || !xp) return st;
   const dim3 ggrid(static_cast<unsigned>((A + 3) / 4));
@@ -276,5 +285,29 @@ extern "C" cle_status cle_dispatch_many(int32_t n, const int32_t* const* topk_id
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return CLE_EWORKSPACE;
   a.hist = static_cast<int*>(ws);
   a.hist_stride = static_cast<int64_t>(one / sizeof(int));
+  a.st = nullptr;
   return launch_dispatch(a, n, A, E, as_stream(stream));
 }
+
+namespace cle {
+
+cle_status launch_dispatch_many(int n, const int* const* idx, int T, int k, int E,
+                                int* const* counts, int* const* offsets, int* const* dest,
+                                int* const* src, void* ws, const cle_loop_state* st,
+                                hipStream_t s) {
+  DispatchArgs a;
+  for (int j = 0; j < n; ++j) {
+    a.idx[j] = idx[j];
+    a.counts[j] = counts[j];
+    a.offsets[j] = offsets[j];
+    a.dest[j] = dest[j];
+    a.src[j] = src[j];
+  }
+  a.hist = static_cast<int*>(ws);
+  a.hist_stride =
+      static_cast<int64_t>(cle_workspace_bytes(CLE_OP_DISPATCH, T, E, k, 0, 1) / sizeof(int));
+  a.st = st;
+  return launch_dispatch(a, n, static_cast<int64_t>(T) * k, E, s);
+}
+
+}  // namespace cle

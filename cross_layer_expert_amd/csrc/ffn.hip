@@ -24,6 +24,8 @@
 // once and crowd the same HBM channels).
 // Consecutive logical tiles go to one XCD (workgroups are dealt round-robin
 // over the 8 XCDs) so tiles reading the same weight rows share that XCD's L2.
+#include <hip/hip_ext.h>
+
 #include "cle_internal.h"
 
 namespace cle {
@@ -62,6 +64,9 @@ struct PlanArgs {
   int nd, seg_base, first;
   int E, ns, H, I, esz;
   int tm, tn1, tn2;  // tile rows, phase-1 act columns, phase-2 output columns
+  // non-NULL: descriptor c + j (c = seg_base / (E + ns)) runs only if it is in
+  // st->runset, at layer st->run_layer[c + j] (its own layer field is unused)
+  const cle_loop_state* st;
 };
 static_assert(sizeof(PlanArgs) <= 4096, "kernel argument size");
 
@@ -73,28 +78,44 @@ __device__ __forceinline__ void seg_range(const DescDev& d, int e, int& lo, int&
   hi = min(max(d.offsets[e + 1], lo), d.rows);
 }
 
-__device__ __forceinline__ int seg_rows(const PlanArgs& p, int s) {
+__device__ __forceinline__ int seg_rows(const PlanArgs& p, const DescDev* dd, int s) {
   const int j = s / (p.E + p.ns), e = s % (p.E + p.ns);
   if (e < p.E) {
     int lo, hi;
-    seg_range(p.d[j], e, lo, hi);
+    seg_range(dd[j], e, lo, hi);
     return hi - lo;
   }
-  return p.d[j].shared_rows;
+  return dd[j].shared_rows;
 }
 
 __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ segs,
                                                  int* __restrict__ totals) {
   __shared__ int s1[1024], s2[1024];
   __shared__ int base1, base2;
+  __shared__ DescDev dd[kPlanDescs];
   const int tid = threadIdx.x;
+  if (tid < p.nd) {
+    DescDev d = p.d[tid];
+    if (p.st) {
+      const int jj = p.seg_base / (p.E + p.ns) + tid;
+      if (p.st->runset >> jj & 1) {
+        d.layer = p.st->run_layer[jj];
+      } else {
+        d.rows = 0;
+        d.shared_rows = 0;
+        d.layer = 0;
+      }
+    }
+    dd[tid] = d;
+  }
+  __syncthreads();
   const int nseg = p.nd * (p.E + p.ns);
   const int per = (nseg + 1023) / 1024;
   const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
   const int n1 = p.I / p.tn1, n2 = p.H / p.tn2;
   int c1 = 0, c2 = 0;
   for (int s = lo; s < hi; ++s) {
-    const int mt = (seg_rows(p, s) + p.tm - 1) / p.tm;
+    const int mt = (seg_rows(p, dd, s) + p.tm - 1) / p.tm;
     c1 += mt * n1;
     c2 += mt * n2;
   }
@@ -117,7 +138,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
   const int64_t H = p.H, I = p.I, esz = p.esz;
   for (int s = lo; s < hi; ++s) {
     const int j = s / (p.E + p.ns), e = s % (p.E + p.ns);
-    const DescDev& d = p.d[j];
+    const DescDev& d = dd[j];
     Seg g;
     if (e < p.E) {
       int lo, hi;
@@ -606,7 +627,17 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
                                              int32_t I, cle_dtype dt, int32_t w_layout, void* ws,
                                              size_t ws_bytes, void* const* phase_events,
                                              void* stream) {
-  using namespace cle;
+  return cle::grouped_ffn(d, n_desc, w13, w2, w13_shared, w2_shared, L, E, n_shared, H, I, dt,
+                          w_layout, ws, ws_bytes, phase_events, nullptr, true, stream);
+}
+
+namespace cle {
+
+cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, const void* w2,
+                       const void* w13_shared, const void* w2_shared, int32_t L, int32_t E,
+                       int32_t n_shared, int32_t H, int32_t I, cle_dtype dt, int32_t w_layout,
+                       void* ws, size_t ws_bytes, void* const* phase_events,
+                       const cle_loop_state* st, bool launch, void* stream) {
   if (!d || n_desc < 1 || n_desc > CLE_MAX_DESC) return CLE_EINVAL;
   if (!w13 || !w2 || L < 1 || E < 1 || E > CLE_MAX_E || n_shared < 0) return CLE_EINVAL;
   if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
@@ -649,6 +680,7 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
   if (ub1 > INT32_MAX || ub2 > INT32_MAX) return CLE_EUNSUPPORTED;
   const size_t need = cle_workspace_bytes(CLE_OP_FFN, 0, E, 1, n_shared, n_desc);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return CLE_EWORKSPACE;
+  if (!launch) return CLE_OK;
 
   hipStream_t s = as_stream(stream);
   int* totals = static_cast<int*>(ws);
@@ -677,59 +709,48 @@ extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_de
     p.tm = tm;
     p.tn1 = tn1;
     p.tn2 = tn2;
+    p.st = st;
     ffn_plan<<<dim3(1), dim3(1024), 0, s>>>(p, segs, totals);
   }
-  if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[0]), s) != hipSuccess)
-    return CLE_EHIP;
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (phase_events)
+    for (int q = 0; q < 4; ++q) ev[q] = static_cast<hipEvent_t>(phase_events[q]);
+  // One persistent launch of `kernel` over `ub` tiles at most; the events (if
+  // any) are taken by the launch itself, so timing adds no marker between
+  // kernels.  A phase without tiles records its event pair back to back.
+  auto run_phase = [&](auto kernel, int* occ, int threads, int64_t ub, hipEvent_t e0,
+                       hipEvent_t e1) -> bool {
+    if (ub > 0) {
+      const int g = persistent_grid(ub, resident_blocks(kernel, occ, threads));
+      hipExtLaunchKernelGGL(kernel, dim3(g), dim3(threads), 0, s, e0, e1, 0,
+                            static_cast<const Seg*>(segs), nseg,
+                            static_cast<const int*>(totals), H, I);
+      return true;
+    }
+    return !e0 || (hipEventRecord(e0, s) == hipSuccess && hipEventRecord(e1, s) == hipSuccess);
+  };
   static int occ_b1[64], occ_b2[64], occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64];
   static int occ_b1p[64], occ_b2p[64], occ_c1p[64], occ_c2p[64];
-  if (ub1 > 0) {
-    if (wide) {
-      if (packed) {
-        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8, 2, true>, occ_b1p, 512));
-        ffn_gemm_bf16<1, 8, 2, true><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
-      } else {
-        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 8, 2, false>, occ_b1, 512));
-        ffn_gemm_bf16<1, 8, 2, false><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
-      }
-    } else if (dt == CLE_BF16) {
-      if (packed) {
-        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4, 2, true>, occ_c1p, 256));
-        ffn_gemm_bf16<1, 4, 2, true><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-      } else {
-        const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_bf16<1, 4, 2, false>, occ_c1, 256));
-        ffn_gemm_bf16<1, 4, 2, false><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-      }
-    } else {
-      const int g = persistent_grid(ub1, resident_blocks(ffn_gemm_f32<1>, occ_f1, 256));
-      ffn_gemm_f32<1><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-    }
-  }
-  if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[1]), s) != hipSuccess)
-    return CLE_EHIP;
-  if (ub2 > 0) {
-    if (wide) {
-      if (packed) {
-        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8, 2, true>, occ_b2p, 512));
-        ffn_gemm_bf16<2, 8, 2, true><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
-      } else {
-        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 8, 2, false>, occ_b2, 512));
-        ffn_gemm_bf16<2, 8, 2, false><<<dim3(g), dim3(512), 0, s>>>(segs, nseg, totals, H, I);
-      }
-    } else if (dt == CLE_BF16) {
-      if (packed) {
-        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4, 2, true>, occ_c2p, 256));
-        ffn_gemm_bf16<2, 4, 2, true><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-      } else {
-        const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_bf16<2, 4, 2, false>, occ_c2, 256));
-        ffn_gemm_bf16<2, 4, 2, false><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-      }
-    } else {
-      const int g = persistent_grid(ub2, resident_blocks(ffn_gemm_f32<2>, occ_f2, 256));
-      ffn_gemm_f32<2><<<dim3(g), dim3(256), 0, s>>>(segs, nseg, totals, H, I);
-    }
-  }
-  if (phase_events && hipEventRecord(static_cast<hipEvent_t>(phase_events[2]), s) != hipSuccess)
-    return CLE_EHIP;
+  bool ok;
+  if (wide)
+    ok = packed ? run_phase(ffn_gemm_bf16<1, 8, 2, true>, occ_b1p, 512, ub1, ev[0], ev[1])
+                : run_phase(ffn_gemm_bf16<1, 8, 2, false>, occ_b1, 512, ub1, ev[0], ev[1]);
+  else if (dt == CLE_BF16)
+    ok = packed ? run_phase(ffn_gemm_bf16<1, 4, 2, true>, occ_c1p, 256, ub1, ev[0], ev[1])
+                : run_phase(ffn_gemm_bf16<1, 4, 2, false>, occ_c1, 256, ub1, ev[0], ev[1]);
+  else
+    ok = run_phase(ffn_gemm_f32<1>, occ_f1, 256, ub1, ev[0], ev[1]);
+  if (!ok) return CLE_EHIP;
+  if (wide)
+    ok = packed ? run_phase(ffn_gemm_bf16<2, 8, 2, true>, occ_b2p, 512, ub2, ev[2], ev[3])
+                : run_phase(ffn_gemm_bf16<2, 8, 2, false>, occ_b2, 512, ub2, ev[2], ev[3]);
+  else if (dt == CLE_BF16)
+    ok = packed ? run_phase(ffn_gemm_bf16<2, 4, 2, true>, occ_c2p, 256, ub2, ev[2], ev[3])
+                : run_phase(ffn_gemm_bf16<2, 4, 2, false>, occ_c2, 256, ub2, ev[2], ev[3]);
+  else
+    ok = run_phase(ffn_gemm_f32<2>, occ_f2, 256, ub2, ev[2], ev[3]);
+  if (!ok) return CLE_EHIP;
   return launch_status();
 }
+
+}  // namespace cle

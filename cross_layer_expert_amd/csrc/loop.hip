@@ -1,0 +1,470 @@
+// Device-driven loop: Algorithm 1 of "EasyBalance: Cross-Layer Load
+// Balancing in Distributed MoE Inference" (§4.2) with Schedule(S, m) run on
+// the device, and the device form of that schedule for callers that keep
+// workloads in device memory.
+//
+// The schedule needs only n x D integers (the paper's "small-sized routing
+// metadata"), so it runs as one workgroup between the dispatch and the
+// expert launch.  A step is then a fixed sequence of launches whose
+// membership masks live in device memory: the host enqueues steps without
+// waiting for the stream.
+//
+// Policies (§4.2 for m; §5.2 for MaxUtil, CumUtil, DiffPeak) follow the
+// readings of the host scheduler exactly: U = sum_d W_d / (D max_d W_d),
+// compared by cross-multiplication (0 for an all-zero workload); CumUtil and
+// DiffPeak scan ids upwards from the first ready one and pad to m with the
+// lowest rejected ids; MaxUtil maximises U over subsets of S with |R| >= m,
+// ties to the larger set, then to the lexicographically smallest sorted ids.
+// The linear scans run on one lane (n, D <= 64); MaxUtil's subsets are
+// spread over the workgroup and reduced with that total order, so the
+// winner does not depend on how the subsets were split.
+#include "cle_internal.h"
+
+namespace cle {
+namespace {
+
+constexpr int kSchedThreads = 1024;
+constexpr int kMaxD = CLE_MAX_LOOP_D;
+constexpr int kMaxN = CLE_MAX_MICROBATCHES;
+
+struct UtilD {
+  int64_t num;  // sum_d W_d
+  int64_t den;  // max_d W_d (1 with num 0 for an all-zero workload)
+};
+
+__device__ __forceinline__ bool util_gt(UtilD a, UtilD b) {
+  return static_cast<__int128>(a.num) * b.den > static_cast<__int128>(b.num) * a.den;
+}
+
+// Shared memory of one schedule: workloads and the MaxUtil reduction.
+struct SchedLDS {
+  int w[kMaxN][kMaxD];
+  int64_t W[kMaxD];
+  int ids[kMaxN];
+  int64_t rnum[kSchedThreads], rden[kSchedThreads];
+  uint64_t rmask[kSchedThreads];
+  int rsize[kSchedThreads];
+  uint64_t result;
+};
+
+__device__ uint64_t pad_to_m(uint64_t chosen, uint64_t ready, int m) {
+  for (int j = 0; j < kMaxN && __popcll(chosen) < m; ++j) {
+    const uint64_t b = 1ull << j;
+    if ((ready & b) && !(chosen & b)) chosen |= b;
+  }
+  return chosen;
+}
+
+__device__ UtilD util_of_lds(const int64_t* W, int D) {
+  int64_t s = 0, mx = 0;
+  for (int d = 0; d < D; ++d) {
+    s += W[d];
+    mx = W[d] > mx ? W[d] : mx;
+  }
+  return mx == 0 ? UtilD{0, 1} : UtilD{s, mx};
+}
+
+// One lane: CumUtil.
+__device__ uint64_t cumutil_lane(SchedLDS& L, int n, int D, uint64_t ready, int m) {
+  uint64_t chosen = 0;
+  for (int j = 0; j < n; ++j) {
+    if (!(ready >> j & 1)) continue;
+    if (!chosen) {
+      for (int d = 0; d < D; ++d) L.W[d] = L.w[j][d];
+      chosen = 1ull << j;
+      continue;
+    }
+    int64_t s = 0, mx = 0;
+    for (int d = 0; d < D; ++d) {
+      const int64_t t = L.W[d] + L.w[j][d];
+      s += t;
+      mx = t > mx ? t : mx;
+    }
+    const UtilD ut = mx == 0 ? UtilD{0, 1} : UtilD{s, mx};
+    if (util_gt(ut, util_of_lds(L.W, D))) {
+      for (int d = 0; d < D; ++d) L.W[d] += L.w[j][d];
+      chosen |= 1ull << j;
+    }
+  }
+  return pad_to_m(chosen, ready, m);
+}
+
+// One lane: DiffPeak (peak = lowest index among equal maxima).
+__device__ uint64_t diffpeak_lane(SchedLDS& L, int n, int D, uint64_t ready, int m) {
+  uint64_t chosen = 0, taken = 0;  // taken: bit d = group d is a chosen member's peak
+  for (int j = 0; j < n; ++j) {
+    if (!(ready >> j & 1)) continue;
+    int p = 0;
+    for (int d = 1; d < D; ++d)
+      if (L.w[j][d] > L.w[j][p]) p = d;
+    if (!chosen || !(taken >> p & 1)) {
+      chosen |= 1ull << j;
+      taken |= 1ull << p;
+    }
+  }
+  return pad_to_m(chosen, ready, m);
+}
+
+// a preferred over b (b.size < 0: no candidate yet)?
+__device__ __forceinline__ bool better(UtilD ua, int sa, uint64_t ma, UtilD ub, int sb,
+                                       uint64_t mb) {
+  if (sa < 0) return false;
+  if (sb < 0) return true;
+  if (util_gt(ua, ub)) return true;
+  if (util_gt(ub, ua)) return false;
+  if (sa != sb) return sa > sb;
+  const uint64_t diff = ma ^ mb;
+  return diff && ((ma >> __builtin_ctzll(diff)) & 1);
+}
+
+// Whole workgroup: MaxUtil over the subsets of the pool with |R| >= m.
+__device__ void maxutil_block(SchedLDS& L, int D, uint64_t ready, int m) {
+  const int tid = threadIdx.x;
+  const int p = __popcll(ready);
+  if (tid == 0) {
+    int q = 0;
+    for (int j = 0; j < kMaxN; ++j)
+      if (ready >> j & 1) L.ids[q++] = j;
+  }
+  __syncthreads();
+  UtilD bu{0, 1};
+  int bs = -1;
+  uint64_t bm = 0;
+  const uint64_t count = 1ull << p;
+  for (uint64_t i = 1 + tid; i < count; i += kSchedThreads) {
+    const int size = __popcll(i);
+    if (size < m) continue;
+    int64_t s = 0, mx = 0;
+    for (int d = 0; d < D; ++d) {
+      int64_t t = 0;
+      for (uint64_t b = i; b; b &= b - 1) t += L.w[L.ids[__builtin_ctzll(b)]][d];
+      s += t;
+      mx = t > mx ? t : mx;
+    }
+    uint64_t mask = 0;
+    for (uint64_t b = i; b; b &= b - 1) mask |= 1ull << L.ids[__builtin_ctzll(b)];
+    const UtilD u = mx == 0 ? UtilD{0, 1} : UtilD{s, mx};
+    if (better(u, size, mask, bu, bs, bm)) {
+      bu = u;
+      bs = size;
+      bm = mask;
+    }
+  }
+  L.rnum[tid] = bu.num;
+  L.rden[tid] = bu.den;
+  L.rsize[tid] = bs;
+  L.rmask[tid] = bm;
+  __syncthreads();
+  for (int off = kSchedThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      const int o = tid + off;
+      if (better(UtilD{L.rnum[o], L.rden[o]}, L.rsize[o], L.rmask[o],
+                 UtilD{L.rnum[tid], L.rden[tid]}, L.rsize[tid], L.rmask[tid])) {
+        L.rnum[tid] = L.rnum[o];
+        L.rden[tid] = L.rden[o];
+        L.rsize[tid] = L.rsize[o];
+        L.rmask[tid] = L.rmask[o];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) L.result = L.rmask[0];
+  __syncthreads();
+}
+
+// Whole workgroup: RunSet of the pool `ready` (non-zero) from L.w; the result
+// is returned to every thread.
+__device__ uint64_t schedule_block(SchedLDS& L, int n, int D, uint64_t ready, int m, int policy) {
+  const int pool = __popcll(ready);
+  if (policy == CLE_POLICY_MAXUTIL && pool > m) {
+    maxutil_block(L, D, ready, m);
+    return L.result;
+  }
+  if (threadIdx.x == 0) {
+    uint64_t r;
+    switch (policy) {
+      case CLE_POLICY_B0_ALONE: r = ready & (~ready + 1); break;
+      case CLE_POLICY_B1_LOCKSTEP: r = ready; break;
+      case CLE_POLICY_CUMUTIL: r = pool < m ? ready : cumutil_lane(L, n, D, ready, m); break;
+      case CLE_POLICY_DIFFPEAK: r = pool < m ? ready : diffpeak_lane(L, n, D, ready, m); break;
+      default: r = ready; break;  // MAXUTIL with |S| <= m: S itself
+    }
+    L.result = r;
+  }
+  __syncthreads();
+  return L.result;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_w_kernel(const int* __restrict__ w,
+                                                                  int n, int D, uint64_t ready,
+                                                                  int m, int policy,
+                                                                  uint64_t* __restrict__ out) {
+  __shared__ SchedLDS L;
+  for (int i = threadIdx.x; i < n * D; i += kSchedThreads) {
+    const int v = w[i];
+    L.w[i / D][i % D] = v > 0 ? v : 0;
+  }
+  __syncthreads();
+  const uint64_t r = schedule_block(L, n, D, ready, m, policy);
+  if (threadIdx.x == 0) out[0] = r;
+}
+
+struct LoopSchedArgs {
+  const int* counts[kMaxN];
+  cle_loop_state* st;
+  int* w_out;          // [n, D] or NULL
+  uint64_t* log;       // ring or NULL
+  int64_t log_cap;
+  int n, E, D, m, policy, restart;
+};
+
+// One loop step's schedule: workloads from the counts, RunSet, statistics,
+// log, layer advance, pool update and the optional restart.
+__global__ __launch_bounds__(kSchedThreads) void loop_schedule_kernel(LoopSchedArgs a) {
+  __shared__ SchedLDS L;
+  cle_loop_state* st = a.st;
+  const int n = a.n, D = a.D, g = a.E / a.D;
+  const uint64_t ready = st->ready;
+  for (int i = threadIdx.x; i < n * D; i += kSchedThreads) {
+    const int j = i / D, d = i % D;
+    const int* c = a.counts[j] + d * g;
+    int s = 0;
+    for (int e = 0; e < g; ++e) s += c[e];
+    L.w[j][d] = s;
+    if (a.w_out) a.w_out[i] = s;
+  }
+  __syncthreads();
+  uint64_t r = 0;
+  if (ready) r = schedule_block(L, n, D, ready, a.m, a.policy);
+  if (threadIdx.x != 0) return;
+  st->restarted = 0;
+  st->runset = r;
+  if (!r) {
+    st->todo = 0;
+    return;
+  }
+  int64_t sum = 0, mx = 0, sep = 0;
+  for (int d = 0; d < D; ++d) {
+    int64_t t = 0;
+    for (int j = 0; j < n; ++j)
+      if (r >> j & 1) t += L.w[j][d];
+    sum += t;
+    mx = t > mx ? t : mx;
+  }
+  for (int j = 0; j < n; ++j) {
+    if (!(r >> j & 1)) continue;
+    int pk = 0;
+    for (int d = 0; d < D; ++d) pk = L.w[j][d] > pk ? L.w[j][d] : pk;
+    sep += pk;
+  }
+  if (a.log) a.log[st->acc[3] % a.log_cap] = r;
+  st->acc[0] += sum;
+  st->acc[1] += mx;
+  st->acc[2] += sep;
+  st->acc[3] += 1;
+  uint64_t left = ready;
+  for (int j = 0; j < n; ++j) {
+    if (!(r >> j & 1)) continue;
+    st->run_layer[j] = st->layer[j];
+    st->layer[j] += 1;
+    if (st->layer[j] >= st->L) left &= ~(1ull << j);
+  }
+  st->ready = left;
+  st->todo = r & left;
+  if (!left && a.restart) {
+    uint64_t all = 0;
+    for (int j = 0; j < n; ++j) {
+      st->layer[j] = st->start[j];
+      if (st->start[j] < st->L) all |= 1ull << j;
+    }
+    st->ready = all;
+    st->todo = all;
+    st->restarts += 1;
+    st->restarted = 1;
+  }
+}
+
+struct LoopInitArgs {
+  int start[kMaxN];
+  cle_loop_state* st;
+  int n, L;
+};
+
+__global__ void loop_init_kernel(LoopInitArgs a) {
+  cle_loop_state* st = a.st;
+  const int j = threadIdx.x;
+  if (j < kMaxN) {
+    const int s = j < a.n ? a.start[j] : a.L;
+    st->layer[j] = s;
+    st->start[j] = s;
+    st->run_layer[j] = 0;
+  }
+  if (j == 0) {
+    uint64_t ready = 0;
+    for (int q = 0; q < a.n; ++q)
+      if (a.start[q] < a.L) ready |= 1ull << q;
+    st->ready = ready;
+    st->todo = ready;
+    st->runset = 0;
+    for (int q = 0; q < 4; ++q) st->acc[q] = 0;
+    st->n = a.n;
+    st->L = a.L;
+    st->restarts = 0;
+    st->restarted = 0;
+  }
+}
+
+struct RestartArgs {
+  const uint4* h0[kMaxN];
+  uint4* h[kMaxN];
+  const cle_loop_state* st;
+  int64_t vecs;  // 16-byte vectors per micro-batch
+};
+
+// h_j = h0_j for every micro-batch, only in a step that restarted the loop.
+__global__ __launch_bounds__(256) void restart_copy_kernel(RestartArgs a) {
+  if (!a.st->restarted) return;
+  const uint4* __restrict__ src = a.h0[blockIdx.y];
+  uint4* __restrict__ dst = a.h[blockIdx.y];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < a.vecs;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    dst[i] = src[i];
+}
+
+bool valid_policy(int p) { return p >= CLE_POLICY_B0_ALONE && p <= CLE_POLICY_DIFFPEAK; }
+
+}  // namespace
+}  // namespace cle
+
+extern "C" cle_status cle_schedule_step_device(const int32_t* w, int32_t n, int32_t D,
+                                               uint64_t ready_mask, int32_t m, int32_t policy,
+                                               uint64_t* runset, void* stream) {
+  using namespace cle;
+  if (!w || !runset) return CLE_EINVAL;
+  if (n < 1 || n > CLE_MAX_MICROBATCHES || D < 1 || D > CLE_MAX_LOOP_D) return CLE_EINVAL;
+  if (m < 1 || m > n || !valid_policy(policy)) return CLE_EINVAL;
+  if (ready_mask == 0) return CLE_EINVAL;
+  if (n < 64 && (ready_mask >> n) != 0) return CLE_EINVAL;
+  if (policy == CLE_POLICY_MAXUTIL && __builtin_popcountll(ready_mask) > m &&
+      __builtin_popcountll(ready_mask) > CLE_MAX_MAXUTIL_POOL)
+    return CLE_EUNSUPPORTED;
+  schedule_w_kernel<<<dim3(1), dim3(kSchedThreads), 0, as_stream(stream)>>>(w, n, D, ready_mask,
+                                                                          m, policy, runset);
+  return launch_status();
+}
+
+extern "C" cle_status cle_loop_init(cle_loop_state* state, int32_t n, int32_t L,
+                                    const int32_t* start, void* stream) {
+  using namespace cle;
+  if (!state || !aligned(state, 8) || n < 1 || n > CLE_MAX_MICROBATCHES || L < 1)
+    return CLE_EINVAL;
+  LoopInitArgs a;
+  for (int j = 0; j < kMaxN; ++j) a.start[j] = 0;
+  for (int j = 0; j < n; ++j) {
+    const int s = start ? start[j] : 0;
+    if (s < 0 || s > L) return CLE_EINVAL;
+    a.start[j] = s;
+  }
+  a.st = state;
+  a.n = n;
+  a.L = L;
+  loop_init_kernel<<<dim3(1), dim3(64), 0, as_stream(stream)>>>(a);
+  return launch_status();
+}
+
+extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_events,
+                                    void* stream) {
+  using namespace cle;
+  if (!d || !d->state || !aligned(d->state, 8)) return CLE_EINVAL;
+  const int n = d->n, T = d->T, E = d->E, k = d->k, H = d->H, D = d->D, ns = d->n_shared;
+  if (n < 1 || n > CLE_MAX_MICROBATCHES || d->L < 1 || T < 1) return CLE_EINVAL;
+  if (E < 1 || E > CLE_MAX_E || k < 1 || k > E || H < 8 || H % 8 || ns < 0) return CLE_EINVAL;
+  if (D < 1 || D > CLE_MAX_LOOP_D || E % D) return CLE_EINVAL;
+  if (d->m < 1 || d->m > n || !valid_policy(d->policy)) return CLE_EINVAL;
+  if (d->policy == CLE_POLICY_MAXUTIL && n > d->m && n > CLE_MAX_MAXUTIL_POOL)
+    return CLE_EUNSUPPORTED;
+  if (d->dtype != CLE_BF16 && d->dtype != CLE_F32) return CLE_EINVAL;
+  if (d->restart != 0 && d->restart != 1) return CLE_EINVAL;
+  if (d->log && d->log_cap < 1) return CLE_EINVAL;
+  const int64_t A = static_cast<int64_t>(T) * k;
+  if (A > INT32_MAX) return CLE_EUNSUPPORTED;
+  for (int j = 0; j < n; ++j) {
+    if (!d->logits[j] || !d->h[j] || !d->idx[j] || !d->gate[j] || !d->counts[j] ||
+        !d->offsets[j] || !d->dest[j] || !d->src[j] || !d->act[j] || !d->yp[j])
+      return CLE_EINVAL;
+    if (!aligned(d->h[j], 16) || !aligned(d->yp[j], 16)) return CLE_EINVAL;
+    if (ns > 0 && (!d->act_shared[j] || !d->y_shared[j] || !aligned(d->y_shared[j], 16)))
+      return CLE_EINVAL;
+    if (d->restart && (!d->h0[j] || !aligned(d->h0[j], 16))) return CLE_EINVAL;
+  }
+  const size_t need = cle_workspace_bytes(CLE_OP_DISPATCH_MANY, T, E, k, 0, n);
+  if (!d->ws_dispatch || d->ws_dispatch_bytes < need || !aligned(d->ws_dispatch, 256))
+    return CLE_EWORKSPACE;
+  cle_ffn_desc fd[CLE_MAX_MICROBATCHES];
+  for (int j = 0; j < n; ++j) {
+    cle_ffn_desc& q = fd[j];
+    q.layer = 0;  // the planner takes the member's layer from the state
+    q.rows = static_cast<int32_t>(A);
+    q.offsets = d->offsets[j];
+    q.xp = nullptr;
+    q.act = d->act[j];
+    q.yp = d->yp[j];
+    q.shared_rows = ns > 0 ? T : 0;
+    q.x_shared = ns > 0 ? d->h[j] : nullptr;
+    q.act_shared = ns > 0 ? d->act_shared[j] : nullptr;
+    q.y_shared = ns > 0 ? d->y_shared[j] : nullptr;
+    q.x = d->h[j];
+    q.src = d->src[j];
+    q.k = k;
+  }
+  const cle_dtype dt = static_cast<cle_dtype>(d->dtype);
+  cle_status rc = grouped_ffn(fd, n, d->w13, d->w2, d->w13_shared, d->w2_shared, d->L, E, ns, H,
+                              d->I, dt, d->w_layout, d->ws_ffn, d->ws_ffn_bytes, phase_events,
+                              d->state, false, stream);
+  if (rc != CLE_OK) return rc;
+
+  hipStream_t s = as_stream(stream);
+  const cle_loop_state* st = d->state;
+  rc = launch_route(n, d->logits, T, E, k, d->idx, d->gate, st, static_cast<int64_t>(T) * E, s);
+  if (rc != CLE_OK) return rc;
+  rc = launch_dispatch_many(n, d->idx, T, k, E, d->counts, d->offsets, d->dest, d->src,
+                            d->ws_dispatch, st, s);
+  if (rc != CLE_OK) return rc;
+  LoopSchedArgs sa;
+  for (int j = 0; j < n; ++j) sa.counts[j] = d->counts[j];
+  sa.st = d->state;
+  sa.w_out = d->w;
+  sa.log = d->log;
+  sa.log_cap = d->log_cap;
+  sa.n = n;
+  sa.E = E;
+  sa.D = D;
+  sa.m = d->m;
+  sa.policy = d->policy;
+  sa.restart = d->restart;
+  loop_schedule_kernel<<<dim3(1), dim3(kSchedThreads), 0, s>>>(sa);
+  rc = grouped_ffn(fd, n, d->w13, d->w2, d->w13_shared, d->w2_shared, d->L, E, ns, H, d->I, dt,
+                   d->w_layout, d->ws_ffn, d->ws_ffn_bytes, phase_events, st, true, stream);
+  if (rc != CLE_OK) return rc;
+  const void* ysh[CLE_MAX_MICROBATCHES];
+  const void* res[CLE_MAX_MICROBATCHES];
+  for (int j = 0; j < n; ++j) {
+    ysh[j] = ns > 0 ? d->y_shared[j] : nullptr;
+    res[j] = d->h[j];
+  }
+  rc = launch_combine_many(n, const_cast<const void* const*>(reinterpret_cast<void* const*>(d->yp)),
+                           d->dest, d->gate, T, k, H, ns > 0 ? ysh : nullptr, ns, res, d->h, dt,
+                           st, s);
+  if (rc != CLE_OK) return rc;
+  if (d->restart) {
+    RestartArgs ra;
+    for (int j = 0; j < n; ++j) {
+      ra.h0[j] = static_cast<const uint4*>(d->h0[j]);
+      ra.h[j] = static_cast<uint4*>(d->h[j]);
+    }
+    ra.st = st;
+    ra.vecs = static_cast<int64_t>(T) * H * (dt == CLE_BF16 ? 2 : 4) / 16;
+    restart_copy_kernel<<<dim3(64, n), dim3(256), 0, s>>>(ra);
+  }
+  return launch_status();
+}

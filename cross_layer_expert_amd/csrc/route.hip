@@ -14,11 +14,15 @@ namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread block
 
-// Buffers of the micro-batches of one launch (blockIdx.y picks one).
+// Buffers of the micro-batches of one launch (blockIdx.y picks one).  With a
+// loop state, only the micro-batches in its `todo` mask are routed, each at
+// its layer l_j: logits[j] is then the base of [L, T, E].
 struct RouteArgs {
   const float* logits[CLE_MAX_MICROBATCHES];
   int* idx[CLE_MAX_MICROBATCHES];
   float* gate[CLE_MAX_MICROBATCHES];
+  const cle_loop_state* st;
+  int64_t layer_stride;
 };
 
 __device__ __forceinline__ uint32_t ord_bits(float z) {
@@ -45,9 +49,14 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E, int k) {
-  const float* __restrict__ logits = args.logits[blockIdx.y];
-  int* __restrict__ idx = args.idx[blockIdx.y];
-  float* __restrict__ gate = args.gate[blockIdx.y];
+  const int j = blockIdx.y;
+  const float* __restrict__ logits = args.logits[j];
+  if (args.st) {  // uniform over the block
+    if (!(args.st->todo >> j & 1)) return;
+    logits += static_cast<int64_t>(args.st->layer[j]) * args.layer_stride;
+  }
+  int* __restrict__ idx = args.idx[j];
+  float* __restrict__ gate = args.gate[j];
   __shared__ float zsel[kRouteWaves][CLE_MAX_E];
   __shared__ int esel[kRouteWaves][CLE_MAX_E];
   const int wave = threadIdx.x / kWave;
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E
 namespace cle {
 namespace {
 
-cle_status launch_route(const RouteArgs& a, int n, int T, int E, int k, hipStream_t s) {
+cle_status launch_route_args(const RouteArgs& a, int n, int T, int E, int k, hipStream_t s) {
   const dim3 grid((T + kRouteWaves - 1) / kRouteWaves, n), block(256);
   const int vpl = (E + kWave - 1) / kWave;
   if (vpl <= 1)
@@ -118,6 +127,21 @@ cle_status launch_route(const RouteArgs& a, int n, int T, int E, int k, hipStrea
 }
 
 }  // namespace
+
+cle_status launch_route(int n, const float* const* logits, int T, int E, int k, int* const* idx,
+                        float* const* gate, const cle_loop_state* st, int64_t layer_stride,
+                        hipStream_t s) {
+  RouteArgs a;
+  for (int j = 0; j < n; ++j) {
+    a.logits[j] = logits[j];
+    a.idx[j] = idx[j];
+    a.gate[j] = gate[j];
+  }
+  a.st = st;
+  a.layer_stride = layer_stride;
+  return launch_route_args(a, n, T, E, k, s);
+}
+
 }  // namespace cle
 
 extern "C" cle_status cle_route(const float* logits, int32_t T, int32_t E, int32_t k,
@@ -132,12 +156,7 @@ extern "C" cle_status cle_route_many(int32_t n, const float* const* logits, int3
   if (n < 1 || n > CLE_MAX_MICROBATCHES || !logits || !topk_idx || !topk_gate) return CLE_EINVAL;
   if (T < 0 || E < 1 || E > CLE_MAX_E || k < 1 || k > E) return CLE_EINVAL;
   if (T == 0) return CLE_OK;
-  RouteArgs a;
-  for (int j = 0; j < n; ++j) {
+  for (int j = 0; j < n; ++j)
     if (!logits[j] || !topk_idx[j] || !topk_gate[j]) return CLE_EINVAL;
-    a.logits[j] = logits[j];
-    a.idx[j] = topk_idx[j];
-    a.gate[j] = topk_gate[j];
-  }
-  return launch_route(a, n, T, E, k, as_stream(stream));
+  return launch_route(n, logits, T, E, k, topk_idx, topk_gate, nullptr, 0, as_stream(stream));
 }

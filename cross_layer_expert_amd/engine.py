@@ -19,9 +19,11 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BF16, OP_DISPATCH, OP_DISPATCH_MANY, OP_FFN, combine, combine_many, dispatch,
-               dispatch_many, grouped_expert_ffn, ids_of, make_desc, mask_of, route, route_many,
-               schedule_step_raw, workload_stats, workspace_bytes)
+from . import (BF16, LOOP_STATE_BYTES, OP_DISPATCH, OP_DISPATCH_MANY, OP_FFN, W_PACKED,
+               W_ROWMAJOR, LoopDesc, combine, combine_many, dispatch, dispatch_many,
+               grouped_expert_ffn, ids_of, loop_init, loop_step, make_desc, mask_of,
+               read_loop_state, route, route_many, schedule_step_raw, workload_stats,
+               workspace_bytes)
 
 
 class Engine:
@@ -33,7 +35,8 @@ class Engine:
     """
 
     def __init__(self, weights, logits, h0, D, k, policy, m, start_layers=None, stream=None,
-                 fused_gather=True, batched=True, packed=False):
+                 fused_gather=True, batched=True, packed=False, device_loop=False, restart=False,
+                 log_cap=4096):
         self.w13, self.w2, self.w13s, self.w2s = weights
         self.packed = packed  # the weights were written by pack_weights (bf16)
         self.L, self.E, I2, self.H = self.w13.shape
@@ -79,7 +82,54 @@ class Engine:
             max(256, workspace_bytes(OP_FFN, 0, E, 1, self.ns, n)) // 4, dtype=torch.int32,
             device=dev)
         self.descs = [self._desc(j) for j in range(n)]
+        # device_loop: the whole step, schedule included, is one cle_loop_step
+        # call reading its masks from device memory; the host never waits.
+        # restart: when every micro-batch has finished, the loop starts over
+        # from h0 inside the same step (for steady-state timing).
+        self.device_loop = device_loop
+        if device_loop:
+            if not self.batched:
+                raise ValueError("device_loop needs the fused gather")
+            self.restart = bool(restart)
+            self.state = torch.zeros(LOOP_STATE_BYTES // 8 + 1, dtype=torch.int64, device=dev)
+            self.log = torch.zeros(int(log_cap), dtype=torch.int64, device=dev)
+            self.loop_desc = self._loop_desc(D, m)
         self.reset()
+
+    def _loop_desc(self, D, m):
+        d = LoopDesc()
+        d.n, d.L, d.T, d.E, d.k, d.H, d.I = self.n, self.L, self.T, self.E, self.k, self.H, self.I
+        d.D, d.m, d.policy, d.n_shared = D, m, self.policy, self.ns
+        d.dtype = 0 if self.h.dtype == torch.bfloat16 else 1
+        d.w_layout = W_PACKED if self.packed else W_ROWMAJOR
+        d.restart = 1 if self.restart else 0
+        for j in range(self.n):
+            d.logits[j] = self.logits[j].data_ptr()
+            d.h[j] = self.h[j].data_ptr()
+            d.h0[j] = self.h0[j].data_ptr()
+            d.idx[j] = self.idx[j].data_ptr()
+            d.gate[j] = self.gates[j].data_ptr()
+            d.counts[j] = self.counts[j].data_ptr()
+            d.offsets[j] = self.offsets[j].data_ptr()
+            d.dest[j] = self.dest[j].data_ptr()
+            d.src[j] = self.src[j].data_ptr()
+            d.act[j] = self.act[j].data_ptr()
+            d.yp[j] = self.yp[j].data_ptr()
+            if self.ns:
+                d.act_shared[j] = self.act_sh[j].data_ptr()
+                d.y_shared[j] = self.y_sh[j].data_ptr()
+        d.w13, d.w2 = self.w13.data_ptr(), self.w2.data_ptr()
+        d.w13_shared = None if self.w13s is None else self.w13s.data_ptr()
+        d.w2_shared = None if self.w2s is None else self.w2s.data_ptr()
+        d.ws_dispatch = self.ws_dispatch.data_ptr()
+        d.ws_dispatch_bytes = self.ws_dispatch.numel() * 4
+        d.ws_ffn = self.ws_ffn.data_ptr()
+        d.ws_ffn_bytes = self.ws_ffn.numel() * 4
+        d.w = self.w_dev.data_ptr()
+        d.log = self.log.data_ptr()
+        d.log_cap = self.log.numel()
+        d.state = self.state.data_ptr()
+        return d
 
     def _desc(self, j):
         if self.fused:
@@ -103,10 +153,36 @@ class Engine:
         self.S = [j for j in range(self.n) if self.l[j] < self.L]
         self.prev = list(self.S)
         self.trace = []
+        if self.device_loop:
+            loop_init(self.state, self.n, self.L, self.start, stream=self.stream)
+            self._logged = 0  # log entries already turned into trace entries
+            self._shadow = list(self.start)
 
     @property
     def done(self) -> bool:
+        if self.device_loop:
+            return read_loop_state(self.state).ready == 0
         return not self.S
+
+    def sync_trace(self):
+        """Device loop: append the RunSets logged since the last call to
+        `trace`, with each member's layer replayed from the starting layers."""
+        st = read_loop_state(self.state)
+        total = int(st.acc[3])
+        if total - self._logged > self.log.numel():
+            raise RuntimeError("RunSet log overwritten: raise log_cap")
+        if total > self._logged:
+            cap = self.log.numel()
+            raw = self.log.cpu().numpy().view(np.uint64)
+            for s in range(self._logged, total):
+                R = ids_of(int(raw[s % cap]))
+                self.trace.append((tuple(R), tuple(self._shadow[j] for j in R)))
+                for j in R:
+                    self._shadow[j] += 1
+                if self.restart and all(v >= self.L for v in self._shadow):
+                    self._shadow = list(self.start)
+            self._logged = total
+        return st
 
     # ------------------------------------------------------------ one step
     def route_dispatch(self, j):
@@ -160,17 +236,32 @@ class Engine:
                     y_shared=None if self.y_sh is None else self.y_sh[j], residual=self.h[j],
                     stream=s)
 
-    def step(self, events=None) -> list:
-        """One iteration of the Algorithm 1 loop; returns RunSet_i."""
+    def step(self, events=None, mark=None) -> list:
+        """One iteration of the Algorithm 1 loop; returns RunSet_i (None with
+        device_loop: the RunSet stays on the device; see sync_trace).
+
+        events: 4 raw hipEvent_t for the expert launch (see grouped_expert_ffn);
+        mark: optional callable, called with 0 / 1 before / after the route +
+        dispatch launches and with 2 after the combine, on the host as the
+        work is enqueued (for timing events on the engine's stream)."""
+        if self.device_loop:
+            loop_step(self.loop_desc, events, stream=self.stream)
+            return None
         todo = [j for j in self.prev if self.l[j] < self.L]
+        if mark:
+            mark(0)
         if self.batched and todo:
             self.route_dispatch_many(todo)
         else:
             for j in todo:
                 self.route_dispatch(j)
+        if mark:
+            mark(1)
         R = self.schedule()
         layers = [self.l[j] for j in R]
         self.moe_compute_combine(R, events=events)
+        if mark:
+            mark(2)
         self.trace.append((tuple(R), tuple(layers)))
         for j in R:
             self.l[j] += 1
@@ -178,14 +269,28 @@ class Engine:
         self.prev = R
         return R
 
-    def run(self):
+    def run(self, chunk=8):
+        """Steps until every micro-batch has finished.  Device loop: steps
+        are enqueued `chunk` at a time between checks of the pool (steps
+        after the last one find it empty and do nothing)."""
+        if self.device_loop:
+            if self.restart:
+                raise ValueError("run() of a restarting loop never ends")
+            while True:
+                for _ in range(chunk):
+                    self.step()
+                if self.sync_trace().ready == 0:
+                    return self
         while self.S:
             self.step()
         return self
 
     def stats(self):
         """(work, effective workload, sum of members' own peaks, steps) and u."""
-        a = [int(v) for v in self.acc.cpu()]
+        if self.device_loop:
+            a = [int(v) for v in read_loop_state(self.state).acc]
+        else:
+            a = [int(v) for v in self.acc.cpu()]
         u = a[0] / (self.D * a[1]) if a[1] else 0.0
         return a, u
 

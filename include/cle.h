@@ -182,9 +182,11 @@ typedef struct {
  *   f32 : fp32 throughout.
  *   w_layout   CLE_W_ROWMAJOR, or CLE_W_PACKED (bf16 only) for all four weight
  *              tensors (see cle_pack_weights).
- *   phase_events: NULL, or HOST array of 3 hipEvent_t recorded on `stream`
- *              after the planning kernel, after the gate/up phase and after
- *              the down phase (for measurement).
+ *   phase_events: NULL, or HOST array of 4 hipEvent_t (for measurement):
+ *              [0], [1] take the start and end of the gate/up kernel, [2], [3]
+ *              those of the down kernel.  They are recorded by the launches
+ *              themselves (no separate marker on `stream`); a phase with no
+ *              tiles records its pair back to back.
  * Rows of each segment are computed with one fixed instruction sequence and
  * a K order that depends only on the segment's layer and expert, so a row's
  * result does not depend on the other segments in the launch.
@@ -287,6 +289,113 @@ cle_status cle_workload_stats(const int32_t* counts, int32_t n, int32_t E, int32
  */
 cle_status cle_schedule_step(const int32_t* w, int32_t n, int32_t D, uint64_t ready_mask,
                              int32_t m, int32_t policy, uint64_t* runset_mask);
+
+/*
+ * cle_schedule_step_device -- cle_schedule_step computed on the device, for
+ * callers that keep the workloads in device memory (no copy to the host and
+ * no wait on the stream).  Same policies, readings and results, bit for bit.
+ *
+ *   w          [n, D] int32 device workloads.
+ *   ready_mask HOST value, as in cle_schedule_step.
+ *   runset     [1] uint64 device out.
+ * Requires cle_schedule_step's conditions on the host-visible arguments,
+ * D <= CLE_MAX_LOOP_D, and n <= CLE_MAX_MAXUTIL_POOL for MAXUTIL (the pool
+ * is only known on the device).  Negative workloads count as 0.
+ */
+#define CLE_MAX_LOOP_D 64
+cle_status cle_schedule_step_device(const int32_t* w, int32_t n, int32_t D, uint64_t ready_mask,
+                                    int32_t m, int32_t policy, uint64_t* runset, void* stream);
+
+/*
+ * The device-driven loop: Algorithm 1 (paper §4.2) with Schedule(S, m)
+ * computed on the device, so a step is a fixed sequence of launches and the
+ * host never waits for the stream between steps.
+ *
+ * cle_loop_state -- the loop's state in DEVICE memory that the caller
+ * allocates (sizeof(cle_loop_state) bytes, 8-byte aligned); written by
+ * cle_loop_init and cle_loop_step, readable by copying it back.
+ */
+typedef struct {
+  int32_t layer[64];      /* l_j: the layer micro-batch j runs next; L once finished */
+  int32_t run_layer[64];  /* the layer at which each member of `runset` ran */
+  int32_t start[64];      /* starting layers (used again by a restart) */
+  uint64_t ready;         /* the pool S: bit j set iff l_j < L */
+  uint64_t todo;          /* routed at the start of the next step: the last RunSet's
+                             members that are still ready (all of S at first: RunSet_0 = S) */
+  uint64_t runset;        /* RunSet of the last step (0 when nothing ran) */
+  int64_t acc[4];         /* as cle_workload_stats' acc, over every step that ran */
+  int32_t n, L;
+  int32_t restarts;       /* how many times every micro-batch finished and the loop restarted */
+  int32_t restarted;      /* 1 from a restart until the next step begins */
+} cle_loop_state;
+
+/*
+ * cle_loop_init -- set the state for n micro-batches of an L-layer stack:
+ * l_j = start[j] (HOST array of n, or NULL for all 0), S = {j : l_j < L},
+ * todo = S, runset = 0, acc = 0.  Requires 1 <= n <= CLE_MAX_MICROBATCHES,
+ * L >= 1, 0 <= start[j] <= L.
+ */
+cle_status cle_loop_init(cle_loop_state* state, int32_t n, int32_t L, const int32_t* start,
+                         void* stream);
+
+/*
+ * cle_loop_desc -- everything one loop step touches (HOST struct; the
+ * pointers are device pointers, per micro-batch j < n).  Layouts are those
+ * of cle_route, cle_dispatch (fused row gather: no xp), cle_grouped_expert_ffn
+ * and cle_combine.
+ */
+typedef struct {
+  int32_t n, L, T, E, k, H, I, D, m, policy, n_shared;
+  int32_t dtype;         /* cle_dtype */
+  int32_t w_layout;      /* cle_w_layout */
+  int32_t restart;       /* 1: when every micro-batch has finished, start over
+                            (l_j = start_j, h_j = h0_j) in the same step */
+  const float* logits[64];          /* [L, T, E]: router logits of every layer */
+  void* h[64];                      /* [T, H]: hidden state, updated in place */
+  const void* h0[64];               /* [T, H]: restart source (restart only) */
+  int32_t* idx[64];                 /* [T, k] */
+  float* gate[64];                  /* [T, k] */
+  int32_t* counts[64];              /* [E] */
+  int32_t* offsets[64];             /* [E + 1] */
+  int32_t* dest[64];                /* [T * k] */
+  int32_t* src[64];                 /* [T * k] */
+  void* act[64];                    /* [T * k, I] */
+  void* yp[64];                     /* [T * k, H] */
+  void* act_shared[64];             /* [n_shared, T, I] (n_shared > 0) */
+  void* y_shared[64];               /* [n_shared, T, H] (n_shared > 0) */
+  const void* w13;                  /* [L, E, 2I, H] */
+  const void* w2;                   /* [L, E, H, I] */
+  const void* w13_shared;           /* [L, n_shared, 2I, H] or NULL */
+  const void* w2_shared;            /* [L, n_shared, H, I] or NULL */
+  void* ws_dispatch;                /* CLE_OP_DISPATCH_MANY workspace, n_desc = n */
+  size_t ws_dispatch_bytes;
+  void* ws_ffn;                     /* CLE_OP_FFN workspace, n_desc = n */
+  size_t ws_ffn_bytes;
+  int32_t* w;                       /* [n, D] out or NULL: workloads the last schedule saw */
+  uint64_t* log;                    /* NULL, or a ring of log_cap RunSet masks: the step that
+                                       ran as the s-th (acc[3] = s before it) writes entry
+                                       s % log_cap */
+  int64_t log_cap;
+  cle_loop_state* state;
+} cle_loop_desc;
+
+/*
+ * cle_loop_step -- enqueue one iteration of Algorithm 1 on `stream`:
+ *   1. route and dispatch the micro-batches in state->todo, each at its l_j;
+ *   2. on the device: w[j][d] for j in S, RunSet = Schedule(S, m) as in
+ *      cle_schedule_step, acc as in cle_workload_stats, the log entry,
+ *      run_layer = l_j and l_j += 1 for the members, S and todo updated
+ *      (and the restart, if asked for and S became empty);
+ *   3. the grouped expert FFN of every member at its run_layer (as
+ *      cle_grouped_expert_ffn, whose phase_events it takes);
+ *   4. h_j = h_j + combine (Eq. (1)) for every member;
+ *   5. on a restart, h_j = h0_j for every j.
+ * A step with S empty (and no restart) does nothing.  Results, state and
+ * statistics are bitwise those of the host-driven sequence of the same calls.
+ * Requires the conditions of the calls above, E % D == 0, D <= CLE_MAX_LOOP_D,
+ * 1 <= m <= n, and n <= CLE_MAX_MAXUTIL_POOL for MAXUTIL.
+ */
+cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_events, void* stream);
 
 /*
  * cle_workspace_bytes -- device workspace, in bytes, that `op` needs:

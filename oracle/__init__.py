@@ -25,5 +25,5 @@ Pinning status of every function is listed in each module's header.
 """
 from .moe import route, dispatch, swiglu_expert, expert_ffn, combine, widen  # noqa: F401
 from .balance import (group_workload, effective_workload, utilization, step_stats,  # noqa: F401
-                      util_of, schedule, POLICIES)
+                      util_of, schedule, same_peak_windows, POLICIES)
 from .engine import run_schedule_only, run_engine, moe_layer  # noqa: F401

@@ -6,6 +6,7 @@ Pins (tests/test_oracle_balance.py):
   the sum-of-max inequality of [PAPER] §4.1 on random workloads; an
   independent closed form of Eq. (3) on per-layer steps; u of any schedule is
   at least u of the one-(micro-batch, layer)-per-step baseline.
+* same_peak_windows -- hand-counted sequences (tests/test_oracle_balance.py).
 * schedule -- hand-worked examples (tests/golden/schedule_examples.json) whose
   expected picks are derived by hand there; MaxUtil against an independent
   brute force (exhaustive ``itertools`` search with a different tie-break
@@ -81,6 +82,25 @@ def utilization(steps_W, D: int) -> Fraction:
     num = sum(sum(int(v) for v in W) for W in steps_W)
     den = sum(max(int(v) for v in W) for W in steps_W)
     return Fraction(num, D * den)
+
+
+def same_peak_windows(w_layers, run: int) -> tuple:
+    """(hits, windows) of the [PAPER] Table 2 statistic for one workload sequence.
+
+    w_layers: the per-layer workload vectors of one micro-batch, in layer
+    order.  A window is ``run`` consecutive layers; it is a hit when every
+    layer in it has the same peak device.  [PAPER] §1 and §4.1 explain why
+    such windows are rare (a hot device in one layer is seldom hot in the
+    next).  Readings: the peak device is the lowest index among equal maxima
+    (as DiffPeak), and windows are counted per micro-batch.
+    """
+    peaks = [_argmax_low(w) for w in w_layers]
+    windows = max(0, len(peaks) - run + 1)
+    hits = 0
+    for s in range(windows):
+        if all(peaks[s + q] == peaks[s] for q in range(run)):
+            hits += 1
+    return hits, windows
 
 
 # ---------------------------------------------------------------- policies

@@ -22,7 +22,8 @@ def test_every_declared_symbol_is_exported():
                               re.M))
     assert {"cle_route", "cle_dispatch", "cle_grouped_expert_ffn", "cle_combine",
             "cle_workload_stats", "cle_schedule_step", "cle_workspace_bytes",
-            "cle_route_many", "cle_dispatch_many", "cle_combine_many"} <= declared
+            "cle_route_many", "cle_dispatch_many", "cle_combine_many", "cle_pack_weights",
+            "cle_schedule_step_device", "cle_loop_init", "cle_loop_step"} <= declared
     for name in declared:
         assert hasattr(cle._lib, name), name
     assert cle.version().count(".") == 2
@@ -185,3 +186,95 @@ def test_maxutil_large_pool_matches_oracle():
         got = cle.ids_of(cle.schedule_step(w, (1 << n) - 1, 12, cle.POLICY_MAXUTIL))
         want = list(oracle.schedule([list(r) for r in w], range(n), 12, oracle.POLICIES["maxutil"]))
         assert got == want
+
+
+def test_loop_structs_match_header(tmp_path):
+    """The ctypes mirrors of cle_loop_state and cle_loop_desc have the C
+    layout: every field offset and both sizes, from a C program built with
+    the system compiler against include/cle.h."""
+    import ctypes
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = []
+    for cname, py in (("cle_loop_state", cle.LoopState), ("cle_loop_desc", cle.LoopDesc)):
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"cle.h\"\n"
+                   "int main(void) {\n" + "\n".join(lines) + "\nreturn 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                               text=True).stdout.splitlines():
+        c, f, v = line.split()
+        got[(c, f)] = int(v)
+    for cname, py in (("cle_loop_state", cle.LoopState), ("cle_loop_desc", cle.LoopDesc)):
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_loop_calls_validate_on_host():
+    """cle_loop_init / cle_loop_step / cle_schedule_step_device reject bad
+    arguments before anything is enqueued."""
+    import ctypes
+    L = cle._lib
+    i32 = ctypes.c_int32
+    assert L.cle_loop_init(None, 4, 8, None, None) == cle.EINVAL            # no state
+    assert L.cle_loop_init(4, 4, 8, None, None) == cle.EINVAL               # unaligned
+    assert L.cle_loop_init(256, 0, 8, None, None) == cle.EINVAL             # n < 1
+    assert L.cle_loop_init(256, 65, 8, None, None) == cle.EINVAL            # n > 64
+    assert L.cle_loop_init(256, 2, 8, (i32 * 2)(0, 9), None) == cle.EINVAL  # start > L
+    assert L.cle_loop_step(None, None, None) == cle.EINVAL
+
+    def desc(**over):
+        d = cle.LoopDesc()
+        d.n, d.L, d.T, d.E, d.k, d.H, d.I, d.D, d.m = 2, 4, 16, 8, 2, 128, 64, 4, 1
+        d.policy, d.dtype, d.w_layout = cle.POLICY_CUMUTIL, cle.BF16, cle.W_ROWMAJOR
+        for f in ("logits", "h", "h0", "idx", "gate", "counts", "offsets", "dest", "src",
+                  "act", "yp"):
+            arr = getattr(d, f)
+            for j in range(2):
+                arr[j] = 4096 * (j + 1)
+        d.w13, d.w2, d.state = 1 << 20, 1 << 21, 1 << 22
+        d.ws_dispatch, d.ws_dispatch_bytes = 1 << 23, 1 << 20
+        d.ws_ffn, d.ws_ffn_bytes = 1 << 24, 1 << 20
+        for k, v in over.items():
+            setattr(d, k, v)
+        return d
+
+    def step(d):
+        return L.cle_loop_step(ctypes.byref(d), None, None)
+
+    assert step(desc(n=0)) == cle.EINVAL
+    assert step(desc(D=3)) == cle.EINVAL                      # E % D
+    assert step(desc(D=128, E=128, k=2)) == cle.EINVAL        # D > 64
+    assert step(desc(m=3)) == cle.EINVAL                      # m > n
+    assert step(desc(policy=7)) == cle.EINVAL
+    assert step(desc(restart=2)) == cle.EINVAL
+    assert step(desc(I=96)) == cle.EINVAL                     # I % 64 (expert launch)
+    assert step(desc(state=None)) == cle.EINVAL
+    assert step(desc(ws_dispatch_bytes=0)) == cle.EWORKSPACE
+    assert step(desc(ws_ffn_bytes=0)) == cle.EWORKSPACE
+    assert step(desc(log=1 << 25, log_cap=0)) == cle.EINVAL
+    d = desc()
+    d.yp[1] = None
+    assert step(d) == cle.EINVAL                              # NULL entry
+    d = desc(n_shared=1)
+    assert step(d) == cle.EINVAL                              # shared buffers missing
+    d = desc(n=21, m=1, policy=cle.POLICY_MAXUTIL)
+    assert step(d) == cle.EUNSUPPORTED                        # MaxUtil pool > 20
+    # cle_schedule_step_device(w, n, D, ready, m, policy, runset, stream)
+    S = L.cle_schedule_step_device
+    assert S(None, 2, 2, 3, 1, 2, 256, None) == cle.EINVAL
+    assert S(256, 2, 65, 3, 1, 2, 256, None) == cle.EINVAL    # D > 64
+    assert S(256, 2, 2, 0, 1, 2, 256, None) == cle.EINVAL     # empty pool
+    assert S(256, 2, 2, 4, 1, 2, 256, None) == cle.EINVAL     # bit beyond n
+    assert S(256, 2, 2, 3, 3, 2, 256, None) == cle.EINVAL     # m > n
+    assert S(256, 21, 2, (1 << 21) - 1, 1, 3, 256, None) == cle.EUNSUPPORTED

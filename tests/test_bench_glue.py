@@ -1,0 +1,31 @@
+"""The host glue bench.py uses for its 1-u figures and sweeps, against the
+oracle: the schedule-only run (library scheduler) and the Table 2 same-peak
+count.  CPU only (the scheduler is host code)."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+
+
+@pytest.mark.parametrize("policy", sorted(oracle.POLICIES))
+@pytest.mark.parametrize("m,start", [(1, None), (2, None), (3, (0, 2, 5, 1, 0))])
+def test_schedule_only_matches_oracle(policy, m, start):
+    rng = np.random.default_rng(len(policy) * 10 + m)
+    n, L, D = 5, 7, 4
+    wt = rng.integers(0, 50, size=(n, L, D))
+    wt[1, 3] = 0                                  # an empty micro-batch at one layer
+    om, steps, _ = bench.schedule_only_u(wt, D, oracle.POLICIES[policy], m, start)
+    trace, _, u = oracle.run_schedule_only([[list(r) for r in wj] for wj in wt], n, L, D, m,
+                                           oracle.POLICIES[policy], start_layers=start)
+    assert steps == len(trace)
+    assert abs(om - (1 - float(u))) < 1e-12
+
+
+def test_same_peak_matches_oracle():
+    rng = np.random.default_rng(3)
+    for D in (2, 4, 8):
+        wt = rng.integers(0, 6, size=(6, 48, D))     # small values: many ties
+        for run in (1, 2, 3):
+            ref = [oracle.same_peak_windows(list(wj), run) for wj in wt]
+            assert bench.same_peak(wt, run) == (sum(h for h, _ in ref), sum(w for _, w in ref))

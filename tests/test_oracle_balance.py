@@ -149,3 +149,34 @@ def test_any_schedule_not_worse_than_per_layer_baseline():
 
     walk((0, 0, 0), [])
     assert seen > 1000
+
+
+def test_same_peak_windows_hand_counted():
+    """Table 2 statistic on a hand-counted sequence.  Peaks per layer:
+    0, 0, 1, 0 (a tie, lowest index), 0.  Pairs: (0,0) hit, (0,1), (1,0),
+    (0,0) hit -> 2 of 4.  Triples: none of 3.  Single layers: 5 of 5."""
+    w = [[5, 1], [6, 2], [1, 7], [3, 3], [9, 0]]
+    assert oracle.same_peak_windows(w, 2) == (2, 4)
+    assert oracle.same_peak_windows(w, 3) == (0, 3)
+    assert oracle.same_peak_windows(w, 1) == (5, 5)
+    assert oracle.same_peak_windows(w[:1], 2) == (0, 0)
+    # one device hot on every layer: every window is a hit
+    assert oracle.same_peak_windows([[0, 4, 1]] * 6, 3) == (4, 4)
+
+
+def test_same_peak_windows_independent_layers():
+    """Layers whose peak device is uniform and independent: the pair rate is
+    1/D and the triple rate 1/D^2 (binomial bounds, 6 sigma)."""
+    rng = np.random.default_rng(11)
+    D, L, reps = 8, 48, 400
+    hits2 = win2 = hits3 = win3 = 0
+    for _ in range(reps):
+        peaks = rng.integers(0, D, L)
+        w = [[10 if d == p else int(rng.integers(0, 10)) for d in range(D)] for p in peaks]
+        h, n = oracle.same_peak_windows(w, 2)
+        hits2, win2 = hits2 + h, win2 + n
+        h, n = oracle.same_peak_windows(w, 3)
+        hits3, win3 = hits3 + h, win3 + n
+    assert win2 == reps * (L - 1) and win3 == reps * (L - 2)
+    for hits, n, p in ((hits2, win2, 1 / D), (hits3, win3, 1 / D ** 2)):
+        assert abs(hits / n - p) <= 6 * (p * (1 - p) / n) ** 0.5, (hits, n, p)
