@@ -55,7 +55,9 @@ extern "C" size_t cle_workspace_bytes(int32_t op, int32_t T, int32_t E, int32_t 
   if (op == CLE_OP_FFN) {
     if (E < 1 || E > CLE_MAX_E || n_shared < 0 || n_desc < 1 || n_desc > CLE_MAX_DESC) return 0;
     size_t segs = static_cast<size_t>(n_desc) * (E + n_shared);
-    return round_up(cle::kFfnHeader + segs * sizeof(cle::Seg), 256);
+    // header, segment table, row-tile prefix of the segments (segs + 1)
+    return round_up(cle::kFfnHeader + segs * sizeof(cle::Seg) + (segs + 1) * sizeof(int32_t),
+                    256);
   }
   return 0;
 }

@@ -67,19 +67,28 @@ constexpr int kDispatchChunk = 1024;  // assignments per histogram block
 inline int64_t dispatch_chunks(int64_t A) { return (A + kDispatchChunk - 1) / kDispatchChunk; }
 
 // FFN workspace: segment table + totals.
+// One (micro-batch, expert) segment of a grouped expert launch.  Segments
+// are stored grouped by (layer, expert): the segments of the micro-batches at
+// the same layer using the same expert sit next to each other, ordered by
+// micro-batch, and a group's tiles are ordered by column tile, then by the
+// group's row tiles, so the tiles that read one block of weight rows run
+// back to back (on one XCD) whichever micro-batch their rows come from.
 struct Seg {
   const uint16_t* a;    // phase-1 A rows (bf16 or f32 storage; byte pointer semantics by dtype)
   void* act;            // phase-1 output / phase-2 A rows
   void* y;              // phase-2 output rows
-  const void* w13;      // [2I, H]
-  const void* w2;       // [H, I]
   const int32_t* rmap;  // NULL: A row r is a + r*H; else token rmap[r] / kdiv of a
+  int32_t widx;         // weights: layer * E + e, or -1 - (layer * n_shared + q) (shared q)
   int32_t rows;
-  int32_t t1;           // first phase-1 tile of this segment
-  int32_t t2;           // first phase-2 tile of this segment
+  int32_t m0;           // row tiles of all groups before this segment's group
+  int32_t gmt;          // row tiles of this segment's group
+  int32_t moff;         // row tiles of the group's segments before this one
   int16_t kdiv;
   uint16_t kkey;        // K-order key of the segment's weights (a function of
                         // layer and expert only)
+  int16_t grank;        // position of the segment in its group
+  int16_t gsize;        // segments in the group
+  int32_t pad;
 };
 static_assert(sizeof(Seg) == 64, "Seg layout");
 

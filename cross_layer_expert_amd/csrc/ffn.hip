@@ -57,16 +57,20 @@ struct DescDev {
 
 struct PlanArgs {
   DescDev d[kPlanDescs];
+  int layer_all[CLE_MAX_DESC];  // layer of every descriptor of the launch (no loop state)
+  int c0, nd, n_all;            // descriptors [c0, c0 + nd) of n_all are planned here
+  int E, ns, H, I, esz, L;
+  // non-NULL: descriptor j runs only if it is in st->runset, at layer
+  // st->run_layer[j] (its own layer field and layer_all are unused)
+  const cle_loop_state* st;
+};
+
+// Expert weight tensors of a launch; a segment names its matrices by index.
+struct Weights {
   const void* w13;
   const void* w2;
   const void* w13s;
   const void* w2s;
-  int nd, seg_base, first;
-  int E, ns, H, I, esz;
-  int tm, tn1, tn2;  // tile rows, phase-1 act columns, phase-2 output columns
-  // non-NULL: descriptor c + j (c = seg_base / (E + ns)) runs only if it is in
-  // st->runset, at layer st->run_layer[c + j] (its own layer field is unused)
-  const cle_loop_state* st;
 };
 static_assert(sizeof(PlanArgs) <= 4096, "kernel argument size");
 
@@ -78,28 +82,30 @@ __device__ __forceinline__ void seg_range(const DescDev& d, int e, int& lo, int&
   hi = min(max(d.offsets[e + 1], lo), d.rows);
 }
 
-__device__ __forceinline__ int seg_rows(const PlanArgs& p, const DescDev* dd, int s) {
-  const int j = s / (p.E + p.ns), e = s % (p.E + p.ns);
-  if (e < p.E) {
-    int lo, hi;
-    seg_range(dd[j], e, lo, hi);
-    return hi - lo;
-  }
-  return dd[j].shared_rows;
-}
-
-__global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ segs,
-                                                 int* __restrict__ totals) {
-  __shared__ int s1[1024], s2[1024];
-  __shared__ int base1, base2;
+// Writes the segments of descriptors [c0, c0 + nd) at their grouped
+// positions.  Descriptors are grouped by layer (ascending; micro-batches not
+// in the loop state's RunSet form a last, empty group); within the group of
+// layer u, holding cnt micro-batches of which j is the rank-th, segment
+// (j, e) sits at  base(u) + e * cnt + rank,  base(u) = (E + ns) * (number of
+// descriptors at layers below u).  So the segments of one (layer, expert) are
+// adjacent, ordered by micro-batch.
+__global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ segs) {
   __shared__ DescDev dd[kPlanDescs];
+  __shared__ int lay[CLE_MAX_DESC];
+  __shared__ int pbase[kPlanDescs], pcnt[kPlanDescs], prank[kPlanDescs];
   const int tid = threadIdx.x;
+  if (tid < p.n_all) {
+    if (p.st)
+      lay[tid] = (p.st->runset >> tid & 1) ? p.st->run_layer[tid] : p.L;
+    else
+      lay[tid] = p.layer_all[tid];
+  }
   if (tid < p.nd) {
     DescDev d = p.d[tid];
     if (p.st) {
-      const int jj = p.seg_base / (p.E + p.ns) + tid;
-      if (p.st->runset >> jj & 1) {
-        d.layer = p.st->run_layer[jj];
+      const int j = p.c0 + tid;
+      if (p.st->runset >> j & 1) {
+        d.layer = p.st->run_layer[j];
       } else {
         d.rows = 0;
         d.shared_rows = 0;
@@ -109,36 +115,23 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
     dd[tid] = d;
   }
   __syncthreads();
-  const int nseg = p.nd * (p.E + p.ns);
-  const int per = (nseg + 1023) / 1024;
-  const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
-  const int n1 = p.I / p.tn1, n2 = p.H / p.tn2;
-  int c1 = 0, c2 = 0;
-  for (int s = lo; s < hi; ++s) {
-    const int mt = (seg_rows(p, dd, s) + p.tm - 1) / p.tm;
-    c1 += mt * n1;
-    c2 += mt * n2;
+  if (tid < p.nd) {
+    const int j = p.c0 + tid, u = lay[j];
+    int below = 0, cnt = 0, rank = 0;
+    for (int q = 0; q < p.n_all; ++q) {
+      below += lay[q] < u;
+      cnt += lay[q] == u;
+      rank += lay[q] == u && q < j;
+    }
+    pbase[tid] = below * (p.E + p.ns);
+    pcnt[tid] = cnt;
+    prank[tid] = rank;
   }
-  if (tid == 0) {
-    base1 = p.first ? 0 : totals[0];
-    base2 = p.first ? 0 : totals[1];
-  }
-  s1[tid] = c1;
-  s2[tid] = c2;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int a1 = tid >= off ? s1[tid - off] : 0;
-    const int a2 = tid >= off ? s2[tid - off] : 0;
-    __syncthreads();
-    s1[tid] += a1;
-    s2[tid] += a2;
-    __syncthreads();
-  }
-  int t1 = base1 + s1[tid] - c1, t2 = base2 + s2[tid] - c2;
   const int64_t H = p.H, I = p.I, esz = p.esz;
-  for (int s = lo; s < hi; ++s) {
-    const int j = s / (p.E + p.ns), e = s % (p.E + p.ns);
-    const DescDev& d = dd[j];
+  for (int s = tid; s < p.nd * (p.E + p.ns); s += 1024) {
+    const int jl = s / (p.E + p.ns), e = s % (p.E + p.ns);
+    const DescDev& d = dd[jl];
     Seg g;
     if (e < p.E) {
       int lo, hi;
@@ -156,9 +149,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
       }
       g.act = static_cast<char*>(d.act) + off * I * esz;
       g.y = static_cast<char*>(d.yp) + off * H * esz;
-      const int64_t we = static_cast<int64_t>(d.layer) * p.E + e;
-      g.w13 = static_cast<const char*>(p.w13) + we * 2 * I * H * esz;
-      g.w2 = static_cast<const char*>(p.w2) + we * H * I * esz;
+      g.widx = d.layer * p.E + e;
     } else {
       const int64_t q = e - p.E, R = d.shared_rows;
       g.rows = d.shared_rows;
@@ -167,35 +158,91 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
       g.kdiv = 1;
       g.act = static_cast<char*>(d.act_shared) + q * R * I * esz;
       g.y = static_cast<char*>(d.y_shared) + q * R * H * esz;
-      const int64_t we = static_cast<int64_t>(d.layer) * p.ns + q;
-      g.w13 = static_cast<const char*>(p.w13s) + we * 2 * I * H * esz;
-      g.w2 = static_cast<const char*>(p.w2s) + we * H * I * esz;
+      g.widx = -1 - (d.layer * p.ns + static_cast<int>(q));
     }
     g.kkey = static_cast<uint16_t>(d.layer * 7 + e * 5);  // e counts shared experts after E
-    g.t1 = t1;
-    g.t2 = t2;
-    segs[p.seg_base + s] = g;
-    const int mt = (g.rows + p.tm - 1) / p.tm;
-    t1 += mt * n1;
-    t2 += mt * n2;
-  }
-  if (tid == 1023) {
-    totals[0] = t1;
-    totals[1] = t2;
+    g.m0 = g.gmt = g.moff = 0;
+    g.grank = static_cast<int16_t>(prank[jl]);
+    g.gsize = static_cast<int16_t>(pcnt[jl]);
+    g.pad = 0;
+    segs[pbase[jl] + e * pcnt[jl] + prank[jl]] = g;
   }
 }
 
-// Segment owning a tile: the last segment whose first tile is <= tile.
-template <int PHASE>
-__device__ __forceinline__ int find_seg(const Seg* segs, int nseg, int tile) {
+// One block over the grouped segment table: the row-tile prefix M over the
+// segments (mscan[s] = row tiles of segments before s), then per segment its
+// group's start m0 = M at the group's first segment, the group's row tiles
+// gmt and its own offset moff in the group.  Group g of m-tile start m0
+// owns tiles [N * m0, N * (m0 + gmt)) of a phase with N column tiles, in
+// column-tile-major order.
+__global__ __launch_bounds__(1024) void ffn_order(Seg* __restrict__ segs, int nseg, int tm,
+                                                  int n1, int n2, int* __restrict__ totals,
+                                                  int* __restrict__ mscan) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (nseg + 1023) / 1024;
+  const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
+  int c = 0;
+  for (int s = lo; s < hi; ++s) c += (segs[s].rows + tm - 1) / tm;
+  part[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += a;
+    __syncthreads();
+  }
+  int m = part[tid] - c;
+  for (int s = lo; s < hi; ++s) {
+    mscan[s] = m;
+    m += (segs[s].rows + tm - 1) / tm;
+  }
+  if (tid == 1023) {
+    mscan[nseg] = m;
+    totals[0] = n1 * m;
+    totals[1] = n2 * m;
+  }
+  __syncthreads();
+  for (int s = lo; s < hi; ++s) {
+    const int s0 = s - segs[s].grank, s1 = s0 + segs[s].gsize;
+    const int m0 = mscan[s0];
+    segs[s].m0 = m0;
+    segs[s].gmt = mscan[s1] - m0;
+    segs[s].moff = mscan[s] - m0;
+  }
+}
+
+// Tile -> (segment, column tile, row tile) in a phase with N column tiles
+// and tm-row tiles: the group is found by binary search on m0 (the last
+// segment with m0 <= tile / N is its group's last segment), the segment by a
+// walk through the group.
+struct TilePos {
+  int si, nt, mi;
+};
+
+__device__ __forceinline__ TilePos locate_tile(const Seg* segs, int nseg, int tile, int N,
+                                               int tm) {
+  const int x = tile / N;
   int lo = 0, hi = nseg - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    const int t = PHASE == 1 ? segs[mid].t1 : segs[mid].t2;
-    if (t <= tile) lo = mid;
+    if (segs[mid].m0 <= x) lo = mid;
     else hi = mid - 1;
   }
-  return lo;
+  const int m0 = segs[lo].m0, gmt = segs[lo].gmt;
+  const int r = tile - N * m0;
+  const int nt = r / gmt, q = r % gmt;
+  int s = lo - segs[lo].grank;
+  while (q >= segs[s].moff + (segs[s].rows + tm - 1) / tm) ++s;
+  return TilePos{s, nt, q - segs[s].moff};
+}
+
+__device__ __forceinline__ const void* seg_weights(const Weights& w, const Seg& g, int PHASE,
+                                                   int64_t H, int64_t I, int esz) {
+  const int64_t mat = PHASE == 1 ? 2 * I * H : H * I;
+  const void* base = g.widx >= 0 ? (PHASE == 1 ? w.w13 : w.w2) : (PHASE == 1 ? w.w13s : w.w2s);
+  const int64_t idx = g.widx >= 0 ? g.widx : -1 - static_cast<int64_t>(g.widx);
+  return static_cast<const char*>(base) + idx * mat * esz;
 }
 
 __device__ __forceinline__ int logical_tile_base(int grid) {
@@ -484,7 +531,7 @@ template <int PHASE, int WN, int NB, bool PACKED>
 __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restrict__ segs,
                                                             int nseg,
                                                             const int* __restrict__ totals,
-                                                            int H, int I) {
+                                                            Weights wts, int H, int I) {
   static_assert(kMB % WN == 0 && WN * NB <= kBlocks && NB % 2 == 0, "tile shape");
   constexpr int HB = NB / 2;
   const int total = totals[PHASE - 1];
@@ -495,11 +542,12 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
   const int K = PHASE == 1 ? H : I;
 
   for (int tile = logical_tile_base(grid); tile < total; tile += grid) {
-    const int si = find_seg<PHASE>(segs, nseg, tile);
-    const Seg sg = segs[si];
-    const int mt = (sg.rows + kTM - 1) / kTM;
-    const int r = tile - (PHASE == 1 ? sg.t1 : sg.t2);
-    const int nt = r / mt, mi = r % mt;
+    // column tiles of the phase: 16 * NB weight rows per wavefront (phase 1:
+    // half gate, half up rows of 8 * NB act columns)
+    const int ncols = PHASE == 1 ? I / (WN * 8 * NB) : H / (WN * 16 * NB);
+    const TilePos tp = locate_tile(segs, nseg, tile, ncols, kTM);
+    const Seg sg = segs[tp.si];
+    const int nt = tp.nt, mi = tp.mi;
     const int row0 = mi * kTM;
     TileArgs t;
     t.K = K;
@@ -520,7 +568,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
       t.rmap = nullptr;
       t.kdiv = 1;
     }
-    const uint16_t* W = static_cast<const uint16_t*>(PHASE == 1 ? sg.w13 : sg.w2);
+    const uint16_t* W = static_cast<const uint16_t*>(seg_weights(wts, sg, PHASE, H, I, 2));
     int wlo, whi;  // first weight rows of this wavefront's two half groups of blocks
     if (PHASE == 1) {
       wlo = (nt * WN + wave) * (16 * HB);  // gate rows
@@ -556,18 +604,17 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
 // ---------------------------------------------------------------- f32 tiles (exact-order reference path)
 template <int PHASE>
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const Seg* __restrict__ segs, int nseg,
-                                                    const int* __restrict__ totals, int H, int I) {
+                                                    const int* __restrict__ totals, Weights wts,
+                                                    int H, int I) {
   const int total = totals[PHASE - 1];
   const int grid = gridDim.x;
   const int K = PHASE == 1 ? H : I;
   for (int tile = logical_tile_base(grid); tile < total; tile += grid) {
-    const int si = find_seg<PHASE>(segs, nseg, tile);
-    const Seg sg = segs[si];
-    const int mt = (sg.rows + kBM - 1) / kBM;
-    const int r = tile - (PHASE == 1 ? sg.t1 : sg.t2);
-    const int nt = r / mt, mi = r % mt;
+    const TilePos tp = locate_tile(segs, nseg, tile, (PHASE == 1 ? I : H) / kBNF, kBM);
+    const Seg sg = segs[tp.si];
+    const int nt = tp.nt, mi = tp.mi;
     const float* A = static_cast<const float*>(PHASE == 1 ? static_cast<const void*>(sg.a) : sg.act);
-    const float* W = static_cast<const float*>(PHASE == 1 ? sg.w13 : sg.w2);
+    const float* W = static_cast<const float*>(seg_weights(wts, sg, PHASE, H, I, 4));
     for (int e = threadIdx.x; e < kBM * 64; e += blockDim.x) {
       const int row = mi * kBM + e / 64;
       const int col = nt * 64 + e % 64;
@@ -686,6 +733,7 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
   int* totals = static_cast<int*>(ws);
   Seg* segs = reinterpret_cast<Seg*>(static_cast<char*>(ws) + kFfnHeader);
   const int nseg = n_desc * (E + n_shared);
+  int* mscan = reinterpret_cast<int*>(segs + nseg);
   for (int c = 0; c < n_desc; c += kPlanDescs) {
     PlanArgs p;
     p.nd = n_desc - c < kPlanDescs ? n_desc - c : kPlanDescs;
@@ -695,23 +743,20 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
                        n_shared > 0 ? q.shared_rows : 0, q.x_shared, q.act_shared, q.y_shared,
                        q.x, q.src, q.k};
     }
-    p.w13 = w13;
-    p.w2 = w2;
-    p.w13s = w13_shared;
-    p.w2s = w2_shared;
-    p.seg_base = c * (E + n_shared);
-    p.first = c == 0;
+    for (int j = 0; j < CLE_MAX_DESC; ++j) p.layer_all[j] = j < n_desc ? d[j].layer : 0;
+    p.c0 = c;
+    p.n_all = n_desc;
     p.E = E;
     p.ns = n_shared;
     p.H = H;
     p.I = I;
     p.esz = esz;
-    p.tm = tm;
-    p.tn1 = tn1;
-    p.tn2 = tn2;
+    p.L = L;
     p.st = st;
-    ffn_plan<<<dim3(1), dim3(1024), 0, s>>>(p, segs, totals);
+    ffn_plan<<<dim3(1), dim3(1024), 0, s>>>(p, segs);
   }
+  ffn_order<<<dim3(1), dim3(1024), 0, s>>>(segs, nseg, tm, I / tn1, H / tn2, totals, mscan);
+  const Weights wts{w13, w2, w13_shared, w2_shared};
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   if (phase_events)
     for (int q = 0; q < 4; ++q) ev[q] = static_cast<hipEvent_t>(phase_events[q]);
@@ -724,7 +769,7 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
       const int g = persistent_grid(ub, resident_blocks(kernel, occ, threads));
       hipExtLaunchKernelGGL(kernel, dim3(g), dim3(threads), 0, s, e0, e1, 0,
                             static_cast<const Seg*>(segs), nseg,
-                            static_cast<const int*>(totals), H, I);
+                            static_cast<const int*>(totals), wts, H, I);
       return true;
     }
     return !e0 || (hipEventRecord(e0, s) == hipSuccess && hipEventRecord(e1, s) == hipSuccess);
