@@ -60,7 +60,10 @@ __global__ __launch_bounds__(256) void dispatch_count(DispatchArgs args, int64_t
 }
 
 // Turns chunk counts into absolute chunk bases in place and writes counts
-// and offsets.
+// and offsets.  Thread (s, e) of S = 1024 / E slices owns expert e in a
+// contiguous run of chunks, so the chunk counts are read and rewritten by
+// all threads at once: sums per (slice, expert), a prefix over slices, the
+// exclusive scan over experts, then the chunk bases.
 __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs args, int64_t chunks, int E,
                                                       int64_t A) {
   if (skip(args, blockIdx.x)) return;
@@ -68,18 +71,30 @@ __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs args, int64_t
   int* __restrict__ counts = args.counts[blockIdx.x];
   int* __restrict__ offsets = args.offsets[blockIdx.x];
   int* __restrict__ src = args.src[blockIdx.x];
+  __shared__ int ps[1024];  // [slice][expert]: chunk-count sums, then their prefix over slices
   __shared__ int tot[CLE_MAX_E];
   __shared__ int part[1024];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) {
+  const int S = 1024 / E;
+  const int64_t cps = (chunks + S - 1) / S;
+  const int sl = tid / E, e = tid % E;
+  const bool owner = sl < S;
+  const int64_t c0 = owner ? min(chunks, sl * cps) : chunks;
+  const int64_t c1 = owner ? min(chunks, c0 + cps) : chunks;
+  if (owner) {
+    int sum = 0;
+    for (int64_t c = c0; c < c1; ++c) sum += chunk_hist[c * E + e];
+    ps[tid] = sum;
+  }
+  __syncthreads();
+  if (tid < E) {
     int run = 0;
-    for (int64_t c = 0; c < chunks; ++c) {
-      int* p = chunk_hist + c * E + e;
-      const int v = *p;
-      *p = run;
+    for (int q = 0; q < S; ++q) {
+      const int v = ps[q * E + tid];
+      ps[q * E + tid] = run;
       run += v;
     }
-    tot[e] = run;
+    tot[tid] = run;
   }
   __syncthreads();
   // exclusive scan of tot[0..E) with one value per thread (E <= 1024)
@@ -103,8 +118,15 @@ __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs args, int64_t
   __syncthreads();
   if (tid < E) tot[tid] = excl;
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x)
-    for (int64_t c = 0; c < chunks; ++c) chunk_hist[c * E + e] += tot[e];
+  if (owner) {
+    int run = tot[e] + ps[tid];
+    for (int64_t c = c0; c < c1; ++c) {
+      int* p = chunk_hist + c * E + e;
+      const int cnt = *p;
+      *p = run;
+      run += cnt;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter(DispatchArgs args, int64_t A, int E,

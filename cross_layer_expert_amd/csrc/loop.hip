@@ -15,15 +15,18 @@
 // DiffPeak scan ids upwards from the first ready one and pad to m with the
 // lowest rejected ids; MaxUtil maximises U over subsets of S with |R| >= m,
 // ties to the larger set, then to the lexicographically smallest sorted ids.
-// The linear scans run on one lane (n, D <= 64); MaxUtil's subsets are
-// spread over the workgroup and reduced with that total order, so the
-// winner does not depend on how the subsets were split.
+// The linear scans run on one wavefront, lane d holding group d (D <= 64);
+// MaxUtil's subsets are spread over the workgroup and reduced with that
+// total order, so the winner does not depend on how the subsets were split.
 #include "cle_internal.h"
 
 namespace cle {
 namespace {
 
+// MaxUtil spreads its subsets over 1024 threads; the other policies run on
+// one wavefront (a smaller launch with less LDS to set up).
 constexpr int kSchedThreads = 1024;
+constexpr int kScanThreads = 64;
 constexpr int kMaxD = CLE_MAX_LOOP_D;
 constexpr int kMaxN = CLE_MAX_MICROBATCHES;
 
@@ -37,13 +40,13 @@ __device__ __forceinline__ bool util_gt(UtilD a, UtilD b) {
 }
 
 // Shared memory of one schedule: workloads and the MaxUtil reduction.
+template <int NT>
 struct SchedLDS {
   int w[kMaxN][kMaxD];
-  int64_t W[kMaxD];
   int ids[kMaxN];
-  int64_t rnum[kSchedThreads], rden[kSchedThreads];
-  uint64_t rmask[kSchedThreads];
-  int rsize[kSchedThreads];
+  int64_t rnum[NT], rden[NT];
+  uint64_t rmask[NT];
+  int rsize[NT];
   uint64_t result;
 };
 
@@ -55,48 +58,70 @@ __device__ uint64_t pad_to_m(uint64_t chosen, uint64_t ready, int m) {
   return chosen;
 }
 
-__device__ UtilD util_of_lds(const int64_t* W, int D) {
-  int64_t s = 0, mx = 0;
-  for (int d = 0; d < D; ++d) {
-    s += W[d];
-    mx = W[d] > mx ? W[d] : mx;
+// Wavefront reductions (every lane gets the result).
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int off) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += static_cast<int64_t>(shfl_xor64(v, off));
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = shfl_xor64(v, off);
+    v = o > v ? o : v;
   }
-  return mx == 0 ? UtilD{0, 1} : UtilD{s, mx};
+  return v;
+}
+// w[j][lane] as a lane value (0 for lanes past D)
+template <int NT>
+__device__ __forceinline__ int64_t w_lane(const SchedLDS<NT>& L, int j, int D) {
+  const int lane = threadIdx.x % kWave;
+  return lane < D ? L.w[j][lane] : 0;
 }
 
-// One lane: CumUtil.
-__device__ uint64_t cumutil_lane(SchedLDS& L, int n, int D, uint64_t ready, int m) {
+// First wavefront, lane d holding group d: CumUtil.
+template <int NT>
+__device__ uint64_t cumutil_wave(SchedLDS<NT>& L, int n, int D, uint64_t ready, int m) {
   uint64_t chosen = 0;
+  int64_t W = 0;
+  UtilD uw{0, 1};
   for (int j = 0; j < n; ++j) {
     if (!(ready >> j & 1)) continue;
-    if (!chosen) {
-      for (int d = 0; d < D; ++d) L.W[d] = L.w[j][d];
-      chosen = 1ull << j;
-      continue;
-    }
-    int64_t s = 0, mx = 0;
-    for (int d = 0; d < D; ++d) {
-      const int64_t t = L.W[d] + L.w[j][d];
-      s += t;
-      mx = t > mx ? t : mx;
-    }
+    const int64_t t = W + w_lane(L, j, D);
+    const int64_t s = wave_sum(t), mx = static_cast<int64_t>(wave_max(t));
     const UtilD ut = mx == 0 ? UtilD{0, 1} : UtilD{s, mx};
-    if (util_gt(ut, util_of_lds(L.W, D))) {
-      for (int d = 0; d < D; ++d) L.W[d] += L.w[j][d];
+    if (!chosen || util_gt(ut, uw)) {
+      W = t;
+      uw = ut;
       chosen |= 1ull << j;
     }
   }
   return pad_to_m(chosen, ready, m);
 }
 
-// One lane: DiffPeak (peak = lowest index among equal maxima).
-__device__ uint64_t diffpeak_lane(SchedLDS& L, int n, int D, uint64_t ready, int m) {
+// Peak group of micro-batch j (lowest index among equal maxima), on the
+// first wavefront.
+template <int NT>
+__device__ __forceinline__ int peak_wave(const SchedLDS<NT>& L, int j, int D) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t key = lane < D ? (static_cast<uint64_t>(L.w[j][lane]) << 32) |
+                                      static_cast<uint32_t>(kWave - 1 - lane)
+                                : 0;
+  return kWave - 1 - static_cast<int>(wave_max(key) & 0xffffffffu);
+}
+
+// First wavefront: DiffPeak.
+template <int NT>
+__device__ uint64_t diffpeak_wave(SchedLDS<NT>& L, int n, int D, uint64_t ready, int m) {
   uint64_t chosen = 0, taken = 0;  // taken: bit d = group d is a chosen member's peak
   for (int j = 0; j < n; ++j) {
     if (!(ready >> j & 1)) continue;
-    int p = 0;
-    for (int d = 1; d < D; ++d)
-      if (L.w[j][d] > L.w[j][p]) p = d;
+    const int p = peak_wave(L, j, D);
     if (!chosen || !(taken >> p & 1)) {
       chosen |= 1ull << j;
       taken |= 1ull << p;
@@ -118,7 +143,8 @@ __device__ __forceinline__ bool better(UtilD ua, int sa, uint64_t ma, UtilD ub, 
 }
 
 // Whole workgroup: MaxUtil over the subsets of the pool with |R| >= m.
-__device__ void maxutil_block(SchedLDS& L, int D, uint64_t ready, int m) {
+template <int NT>
+__device__ void maxutil_block(SchedLDS<NT>& L, int D, uint64_t ready, int m) {
   const int tid = threadIdx.x;
   const int p = __popcll(ready);
   if (tid == 0) {
@@ -131,7 +157,7 @@ __device__ void maxutil_block(SchedLDS& L, int D, uint64_t ready, int m) {
   int bs = -1;
   uint64_t bm = 0;
   const uint64_t count = 1ull << p;
-  for (uint64_t i = 1 + tid; i < count; i += kSchedThreads) {
+  for (uint64_t i = 1 + tid; i < count; i += NT) {
     const int size = __popcll(i);
     if (size < m) continue;
     int64_t s = 0, mx = 0;
@@ -155,7 +181,7 @@ __device__ void maxutil_block(SchedLDS& L, int D, uint64_t ready, int m) {
   L.rsize[tid] = bs;
   L.rmask[tid] = bm;
   __syncthreads();
-  for (int off = kSchedThreads / 2; off > 0; off >>= 1) {
+  for (int off = NT / 2; off > 0; off >>= 1) {
     if (tid < off) {
       const int o = tid + off;
       if (better(UtilD{L.rnum[o], L.rden[o]}, L.rsize[o], L.rmask[o],
@@ -174,33 +200,37 @@ __device__ void maxutil_block(SchedLDS& L, int D, uint64_t ready, int m) {
 
 // Whole workgroup: RunSet of the pool `ready` (non-zero) from L.w; the result
 // is returned to every thread.
-__device__ uint64_t schedule_block(SchedLDS& L, int n, int D, uint64_t ready, int m, int policy) {
+template <int NT>
+__device__ uint64_t schedule_block(SchedLDS<NT>& L, int n, int D, uint64_t ready, int m,
+                                   int policy) {
   const int pool = __popcll(ready);
-  if (policy == CLE_POLICY_MAXUTIL && pool > m) {
-    maxutil_block(L, D, ready, m);
-    return L.result;
+  if constexpr (NT == kSchedThreads) {  // only the wide launch carries MaxUtil's code
+    if (policy == CLE_POLICY_MAXUTIL && pool > m) {
+      maxutil_block(L, D, ready, m);
+      return L.result;
+    }
   }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < kWave) {  // the first wavefront, lane d for group d
     uint64_t r;
     switch (policy) {
       case CLE_POLICY_B0_ALONE: r = ready & (~ready + 1); break;
       case CLE_POLICY_B1_LOCKSTEP: r = ready; break;
-      case CLE_POLICY_CUMUTIL: r = pool < m ? ready : cumutil_lane(L, n, D, ready, m); break;
-      case CLE_POLICY_DIFFPEAK: r = pool < m ? ready : diffpeak_lane(L, n, D, ready, m); break;
+      case CLE_POLICY_CUMUTIL: r = pool < m ? ready : cumutil_wave(L, n, D, ready, m); break;
+      case CLE_POLICY_DIFFPEAK: r = pool < m ? ready : diffpeak_wave(L, n, D, ready, m); break;
       default: r = ready; break;  // MAXUTIL with |S| <= m: S itself
     }
-    L.result = r;
+    if (threadIdx.x == 0) L.result = r;
   }
   __syncthreads();
   return L.result;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_w_kernel(const int* __restrict__ w,
-                                                                  int n, int D, uint64_t ready,
-                                                                  int m, int policy,
-                                                                  uint64_t* __restrict__ out) {
-  __shared__ SchedLDS L;
-  for (int i = threadIdx.x; i < n * D; i += kSchedThreads) {
+template <int NT>
+__global__ __launch_bounds__(NT) void schedule_w_kernel(const int* __restrict__ w, int n, int D,
+                                                       uint64_t ready, int m, int policy,
+                                                       uint64_t* __restrict__ out) {
+  __shared__ SchedLDS<NT> L;
+  for (int i = threadIdx.x; i < n * D; i += NT) {
     const int v = w[i];
     L.w[i / D][i % D] = v > 0 ? v : 0;
   }
@@ -210,7 +240,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_w_kernel(const int* __
 }
 
 struct LoopSchedArgs {
-  const int* counts[kMaxN];
+  const int* offsets[kMaxN];  // [E + 1] per micro-batch, from the dispatch
   cle_loop_state* st;
   int* w_out;          // [n, D] or NULL
   uint64_t* log;       // ring or NULL
@@ -218,24 +248,48 @@ struct LoopSchedArgs {
   int n, E, D, m, policy, restart;
 };
 
-// One loop step's schedule: workloads from the counts, RunSet, statistics,
-// log, layer advance, pool update and the optional restart.
-__global__ __launch_bounds__(kSchedThreads) void loop_schedule_kernel(LoopSchedArgs a) {
-  __shared__ SchedLDS L;
+// One loop step's schedule: workloads from the expert offsets, RunSet, statistics,
+// log, layer advance, pool update and the optional restart.  The state is
+// read into LDS by many lanes at once; the one lane that updates it then
+// only stores.
+template <int NT>
+__global__ __launch_bounds__(NT) void loop_schedule_kernel(LoopSchedArgs a) {
+  __shared__ SchedLDS<NT> L;
+  __shared__ int lay[kMaxN], beg[kMaxN];
+  __shared__ int64_t acc0[4];
+  __shared__ int nl;
   cle_loop_state* st = a.st;
   const int n = a.n, D = a.D, g = a.E / a.D;
   const uint64_t ready = st->ready;
-  for (int i = threadIdx.x; i < n * D; i += kSchedThreads) {
+  if (threadIdx.x < kMaxN) {
+    lay[threadIdx.x] = st->layer[threadIdx.x];
+    beg[threadIdx.x] = st->start[threadIdx.x];
+    if (threadIdx.x < 4) acc0[threadIdx.x] = st->acc[threadIdx.x];
+    if (threadIdx.x == 4) nl = st->L;
+  }
+  // w[j][d] = offsets[j][(d + 1) g] - offsets[j][d g]: the group's counts
+  // summed by the dispatch scan, two loads per (j, d) lane
+  for (int i = threadIdx.x; i < n * D; i += NT) {
     const int j = i / D, d = i % D;
-    const int* c = a.counts[j] + d * g;
-    int s = 0;
-    for (int e = 0; e < g; ++e) s += c[e];
-    L.w[j][d] = s;
-    if (a.w_out) a.w_out[i] = s;
+    const int* o = a.offsets[j];
+    const int w = o[(d + 1) * g] - o[d * g];
+    L.w[j][d] = w;
+    if (a.w_out) a.w_out[i] = w;
   }
   __syncthreads();
   uint64_t r = 0;
   if (ready) r = schedule_block(L, n, D, ready, a.m, a.policy);
+  if (threadIdx.x >= kWave) return;
+  // Eq. (2)/(3) statistics of the RunSet on the first wavefront (lane d =
+  // group d): W_d summed over the members, each member's own peak
+  int64_t Wd = 0, sep = 0;
+  for (int j = 0; j < n; ++j) {
+    if (!(r >> j & 1)) continue;
+    const int64_t x = w_lane(L, j, D);
+    Wd += x;
+    sep += static_cast<int64_t>(wave_max(x));
+  }
+  const int64_t sum = wave_sum(Wd), mx = static_cast<int64_t>(wave_max(Wd));
   if (threadIdx.x != 0) return;
   st->restarted = 0;
   st->runset = r;
@@ -243,39 +297,26 @@ __global__ __launch_bounds__(kSchedThreads) void loop_schedule_kernel(LoopSchedA
     st->todo = 0;
     return;
   }
-  int64_t sum = 0, mx = 0, sep = 0;
-  for (int d = 0; d < D; ++d) {
-    int64_t t = 0;
-    for (int j = 0; j < n; ++j)
-      if (r >> j & 1) t += L.w[j][d];
-    sum += t;
-    mx = t > mx ? t : mx;
-  }
-  for (int j = 0; j < n; ++j) {
-    if (!(r >> j & 1)) continue;
-    int pk = 0;
-    for (int d = 0; d < D; ++d) pk = L.w[j][d] > pk ? L.w[j][d] : pk;
-    sep += pk;
-  }
-  if (a.log) a.log[st->acc[3] % a.log_cap] = r;
-  st->acc[0] += sum;
-  st->acc[1] += mx;
-  st->acc[2] += sep;
-  st->acc[3] += 1;
+  const int Lyr = nl;
+  if (a.log) a.log[acc0[3] % a.log_cap] = r;
+  st->acc[0] = acc0[0] + sum;
+  st->acc[1] = acc0[1] + mx;
+  st->acc[2] = acc0[2] + sep;
+  st->acc[3] = acc0[3] + 1;
   uint64_t left = ready;
   for (int j = 0; j < n; ++j) {
     if (!(r >> j & 1)) continue;
-    st->run_layer[j] = st->layer[j];
-    st->layer[j] += 1;
-    if (st->layer[j] >= st->L) left &= ~(1ull << j);
+    st->run_layer[j] = lay[j];
+    st->layer[j] = lay[j] + 1;
+    if (lay[j] + 1 >= Lyr) left &= ~(1ull << j);
   }
   st->ready = left;
   st->todo = r & left;
   if (!left && a.restart) {
     uint64_t all = 0;
     for (int j = 0; j < n; ++j) {
-      st->layer[j] = st->start[j];
-      if (st->start[j] < st->L) all |= 1ull << j;
+      st->layer[j] = beg[j];
+      if (beg[j] < Lyr) all |= 1ull << j;
     }
     st->ready = all;
     st->todo = all;
@@ -348,8 +389,12 @@ extern "C" cle_status cle_schedule_step_device(const int32_t* w, int32_t n, int3
   if (policy == CLE_POLICY_MAXUTIL && __builtin_popcountll(ready_mask) > m &&
       __builtin_popcountll(ready_mask) > CLE_MAX_MAXUTIL_POOL)
     return CLE_EUNSUPPORTED;
-  schedule_w_kernel<<<dim3(1), dim3(kSchedThreads), 0, as_stream(stream)>>>(w, n, D, ready_mask,
-                                                                          m, policy, runset);
+  if (policy == CLE_POLICY_MAXUTIL)
+    schedule_w_kernel<kSchedThreads><<<dim3(1), dim3(kSchedThreads), 0, as_stream(stream)>>>(
+        w, n, D, ready_mask, m, policy, runset);
+  else
+    schedule_w_kernel<kScanThreads><<<dim3(1), dim3(kScanThreads), 0, as_stream(stream)>>>(
+        w, n, D, ready_mask, m, policy, runset);
   return launch_status();
 }
 
@@ -431,7 +476,7 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
                             d->ws_dispatch, st, s);
   if (rc != CLE_OK) return rc;
   LoopSchedArgs sa;
-  for (int j = 0; j < n; ++j) sa.counts[j] = d->counts[j];
+  for (int j = 0; j < n; ++j) sa.offsets[j] = d->offsets[j];
   sa.st = d->state;
   sa.w_out = d->w;
   sa.log = d->log;
@@ -442,7 +487,10 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
   sa.m = d->m;
   sa.policy = d->policy;
   sa.restart = d->restart;
-  loop_schedule_kernel<<<dim3(1), dim3(kSchedThreads), 0, s>>>(sa);
+  if (d->policy == CLE_POLICY_MAXUTIL)
+    loop_schedule_kernel<kSchedThreads><<<dim3(1), dim3(kSchedThreads), 0, s>>>(sa);
+  else
+    loop_schedule_kernel<kScanThreads><<<dim3(1), dim3(kScanThreads), 0, s>>>(sa);
   rc = grouped_ffn(fd, n, d->w13, d->w2, d->w13_shared, d->w2_shared, d->L, E, ns, H, d->I, dt,
                    d->w_layout, d->ws_ffn, d->ws_ffn_bytes, phase_events, st, true, stream);
   if (rc != CLE_OK) return rc;
