@@ -273,7 +273,7 @@ def sweep(seed, dev, configs=("qwen3", "moonlight", "taskshift"), ns=(2, 4, 8, 1
             print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None):
+def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None, gate=None, prenorm=True):
     """The CPU oracle on (micro-batch, layer) units of the same workload:
     route, dispatch, float64 SwiGLU experts (numpy matmul) and the combine of
     micro-batch 0 at layers 0, 1, ... until budget_s of oracle time is spent.
@@ -294,8 +294,15 @@ def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None):
                 ws = [oracle.widen(W[q][l].cpu().view(torch.int16).numpy().view(np.uint16), "bf16")
                       for q in (2, 3)]
             x = oracle.widen(h0[j], "bf16")
+            if gate is not None:
+                wg = oracle.widen(gate[0][l].cpu().view(torch.int16).numpy().view(np.uint16),
+                                  "bf16")
+                gb = gate[1][l].cpu().numpy()
             t0 = time.perf_counter()
-            out = oracle.moe_layer(x, logits[j, l], cfg.k, w13, w2, ws[0], ws[1])
+            xin = oracle.rmsnorm(x) if prenorm else x
+            z = (logits[j, l] if gate is None
+                 else oracle.gate_logits(xin, wg, gb).astype(np.float32))
+            out = oracle.moe_layer(x, z, cfg.k, w13, w2, ws[0], ws[1], prenorm=prenorm)
             dt = time.perf_counter() - t0
             assert np.isfinite(out["y"]).all()
             spent += dt
@@ -308,7 +315,9 @@ def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None):
                 kind="oracle",
                 sample=f"{units} (micro-batch, layer) unit(s) of the {cfg.name} workload "
                        f"(micro-batch 0, layers 0..{units - 1}; {done_tok} expert tokens; "
-                       f"route, dispatch, float64 SwiGLU experts, combine); {spent:.1f} s")
+                       f"{'rmsnorm, ' if prenorm else ''}"
+                       f"{'router, ' if gate is not None else ''}route, dispatch, float64 "
+                       f"SwiGLU experts, combine); {spent:.1f} s")
 
 
 def main():
@@ -326,6 +335,12 @@ def main():
     ap.add_argument("--host-loop", action="store_true",
                     help="time the host-driven step (schedule on the host after a wait for the "
                          "workloads) instead of the device-driven one")
+    ap.add_argument("--gate", action="store_true",
+                    help="route from the hidden state through each layer's linear router "
+                         "(+ per-layer expert bias) instead of the given router logits")
+    ap.add_argument("--no-prenorm", action="store_true",
+                    help="experts read the raw hidden state (no RMS-normalised block input; "
+                         "the residual stream then overflows bf16 in the last layers)")
     ap.add_argument("--sweep", action="store_true",
                     help="print the 1-u sweep over n, m/n and D (one JSON line per config and D) "
                          "instead of the timed step")
@@ -365,11 +380,20 @@ def main():
 
     W, lt, ht, logits, h0 = setup(cfg, args.seed, dev)
     stream = torch.cuda.current_stream()
+    prenorm = not args.no_prenorm
+    gate = gate_k = None
+    if args.gate:
+        # routing from the hidden state: each layer's linear router (+ bias)
+        gate = (synth.gate_weights_torch(cfg, args.seed, dev),
+                torch.from_numpy(synth.gate_bias(cfg, args.seed)).to(dev))
+        lt = None
     # bf16: the expert launch reads a packed copy of the weights (a one-time
     # re-layout; results are bitwise those of the row-major weights, which the
     # CPU oracle keeps using)
     packed = cfg.dtype == "bf16"
     Wk = tuple(None if w is None else cle.pack_weights(w) for w in W) if packed else W
+    if gate is not None:
+        gate_k = (cle.pack_weights(gate[0]) if packed else gate[0], gate[1])
     torch.cuda.synchronize()
     K, Wm = args.steps, args.warmup
     C = min(K, 40)
@@ -379,7 +403,7 @@ def main():
     # inside that step
     eng = Engine(Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
                  stream=stream, packed=packed, device_loop=device_loop, restart=device_loop,
-                 log_cap=max(4096, Wm + K + 64))
+                 log_cap=max(4096, Wm + K + 64), gate=gate_k, prenorm=prenorm)
     hip = HipEvents()
 
     def one_step(e, events=None):
@@ -418,7 +442,7 @@ def main():
     # stream time each, so they stay out of the timed steps above)
     hst = eng if not device_loop else Engine(
         Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers, stream=stream,
-        packed=packed)
+        packed=packed, gate=gate_k, prenorm=prenorm)
     for _ in range(5):
         one_step(hst)
     torch.cuda.synchronize()
@@ -451,8 +475,24 @@ def main():
     # algorithmic work of every timed launch (counts recomputed by the library)
     need = sorted({jl for R in steps for jl in R})
     counts_host = {}
-    for (j, l) in need:
-        counts_host[(j, l)] = counts_of(eng, j, l).cpu().numpy()
+    if gate is None:
+        for (j, l) in need:
+            counts_host[(j, l)] = counts_of(eng, j, l).cpu().numpy()
+    else:
+        # routing depends on the hidden state: replay the same steps host-driven
+        # from the start (bitwise the same run) and read each member's counts
+        rep = Engine(Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
+                     stream=stream, packed=packed, gate=gate_k, prenorm=prenorm)
+        replayed = []
+        while len(replayed) < Wm + K:
+            if rep.done:
+                rep.reset()
+            R = rep.step()
+            replayed.append(list(zip(R, [rep.l[j] - 1 for j in R])))
+            for j in R:
+                counts_host.setdefault((j, rep.l[j] - 1), rep.counts[j].cpu().numpy())
+        assert replayed[Wm:] == steps, "replay differs from the timed run"
+        del rep
     B1 = B2 = F1 = F2 = 0.0
     for R in steps:
         b1, b2, f1, f2 = ffn_work(cfg, R, counts_host)
@@ -485,6 +525,10 @@ def main():
     esz = 2 if cfg.dtype == "bf16" else 4
     T, k, H, E, ns = cfg.T, cfg.k, cfg.H, cfg.E, cfg.n_shared
     rd_unit = T * E * 4 + T * k * 8 + T * k * 4 + T * k * 8 + 2 * E * 4
+    if gate is not None:   # router: hidden rows and weights in, logits out and back in
+        rd_unit += T * H * esz + E * H * esz + T * E * 4
+    if prenorm:            # the block input: raw rows in, normalised rows out
+        rd_unit += 2 * T * H * esz
     cb_unit = T * k * H * esz + T * k * 8 + (1 + ns) * T * H * esz + T * H * esz
     rd_ms = [hip.ms(mk[0], mk[1]) for mk, r in zip(marks, routed) if r]
     rd_bytes = sum(len(r) for r in routed) * rd_unit
@@ -512,7 +556,7 @@ def main():
         host_loop_ms_per_step=round(host_ms, 4),
     )
 
-    if not args.no_extras:
+    if not args.no_extras and gate is None:
         # per-(micro-batch, layer) workloads of the whole stack -> 1-u per policy
         w_table = [[None] * cfg.L for _ in range(cfg.n)]
         for j in range(cfg.n):
@@ -527,12 +571,14 @@ def main():
                                                          cfg.start_layers)
             uu[name] = dict(one_minus_u=round(one_minus_u, 4), steps=nsteps)
         extras["under_util"] = uu
+    if not args.no_extras:
         # measured whole runs: cross-layer (timed policy) vs one (j, l) per step
         runs = {}
         for name, pol, mm in (("b0", cle.POLICY_B0_ALONE, 1), (args.policy, policy, m)):
             for dl in (False, True):
                 e2 = Engine(Wk, lt, ht, cfg.D, cfg.k, pol, mm, start_layers=cfg.start_layers,
-                            stream=stream, packed=packed, device_loop=dl)
+                            stream=stream, packed=packed, device_loop=dl, gate=gate_k,
+                            prenorm=prenorm)
                 e2.step()
                 e2.reset()
                 torch.cuda.synchronize()
@@ -547,8 +593,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, W, logits, h0, args.cpu_budget)
-        cpu["one_core"] = cpu_baseline(cfg, W, logits, h0, args.cpu_budget / 2, threads=1)
+        cpu = cpu_baseline(cfg, W, logits, h0, args.cpu_budget, gate=gate, prenorm=prenorm)
+        cpu["one_core"] = cpu_baseline(cfg, W, logits, h0, args.cpu_budget / 2, threads=1,
+                                       gate=gate, prenorm=prenorm)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "expert tokens/s", "n_gpus": 1,
@@ -557,6 +604,10 @@ def main():
         "data": "synthetic (seeded router logits with Zipf skew, N(0,1) hidden, N(0,0.02) weights)",
         "config": {"workload": workload_name(cfg), "policy": args.policy if policy != 1 else "b1",
                    "schedule": "device" if device_loop else "host",
+                   "routing": "hidden state through the router" if gate is not None
+                   else "given router logits",
+                   "block": "pre-norm (experts read RMS-normalised rows)" if prenorm
+                   else "raw hidden state",
                    "m": m, "seed": args.seed, "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu,
     }

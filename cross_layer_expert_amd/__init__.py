@@ -74,7 +74,8 @@ class LoopDesc(ctypes.Structure):
                [("w13", _vp), ("w2", _vp), ("w13_shared", _vp), ("w2_shared", _vp),
                 ("ws_dispatch", _vp), ("ws_dispatch_bytes", _sz), ("ws_ffn", _vp),
                 ("ws_ffn_bytes", _sz), ("w", _vp), ("log", _vp), ("log_cap", _i64),
-                ("state", _vp)]
+                ("state", _vp), ("w_gate", _vp), ("gate_bias", _vp), ("gate_logits", _P64),
+                ("prenorm", _i32), ("norm_eps", ctypes.c_float), ("xn", _P64)]
 
 
 LOOP_STATE_BYTES = ctypes.sizeof(LoopState)
@@ -83,6 +84,9 @@ _sig = {
     "cle_schedule_step_device": (_i32, [_vp, _i32, _i32, _u64, _i32, _i32, _vp, _vp]),
     "cle_loop_init": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_i32), _vp]),
     "cle_loop_step": (_i32, [ctypes.POINTER(LoopDesc), ctypes.POINTER(_vp), _vp]),
+    "cle_gate_logits_many": (_i32, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
+                                    _vp]),
+    "cle_rmsnorm_many": (_i32, [_i32, _vp, _vp, _i32, _i32, ctypes.c_float, _i32, _vp]),
     "cle_route": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "cle_route_many": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "cle_dispatch_many": (_i32, [_i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -176,6 +180,30 @@ def route_many(logits, k, topk_idx, topk_gate, stream=None):
     T, E = logits[0].shape
     _check("cle_route_many", _lib.cle_route_many(
         n, _ptrs(logits), T, E, k, _ptrs(topk_idx), _ptrs(topk_gate), _stream(stream)))
+
+
+NORM_EPS = 1e-6
+
+
+def rmsnorm_many(x, y, eps=NORM_EPS, stream=None):
+    """y_j = x_j / sqrt(mean(x_j^2, rows) + eps); lists of [T, H] tensors."""
+    n = len(x)
+    T, H = x[0].shape
+    _check("cle_rmsnorm_many", _lib.cle_rmsnorm_many(n, _ptrs(x), _ptrs(y), T, H, float(eps),
+                                                     _dt(x[0]), _stream(stream)))
+
+
+def gate_logits_many(x, w_gate, logits, bias=None, packed=False, stream=None):
+    """Router logits z_j = x_j w_gate_j^T + bias_j.  x: list of [T, H]; w_gate:
+    list of [E, H] (each micro-batch's layer; packed=True if written by
+    pack_weights); logits: list of [T, E] float32 out; bias: None or a list
+    of [E] float32 tensors (entries may be None)."""
+    n = len(x)
+    T, H = x[0].shape
+    E = w_gate[0].shape[0]
+    _check("cle_gate_logits_many", _lib.cle_gate_logits_many(
+        n, _ptrs(x), _ptrs(w_gate), None if bias is None else _ptrs(bias), T, H, E, _dt(x[0]),
+        W_PACKED if packed else W_ROWMAJOR, _ptrs(logits), _stream(stream)))
 
 
 def dispatch_many(topk_idx, E, counts, offsets, dest, src, ws, stream=None):

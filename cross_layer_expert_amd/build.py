@@ -25,7 +25,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-obj
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 SOURCES = ["abi.cpp", "schedule.cpp", "route.hip", "dispatch.hip", "stats.hip", "combine.hip",
-           "loop.hip",
+           "loop.hip", "norm.hip",
            "ffn.hip", "pack.hip"]
 
 

@@ -36,6 +36,15 @@ cle_status launch_combine_many(int n, const void* const* yp, const int* const* d
                                const void* const* y_shared, int n_shared,
                                const void* const* residual, void* const* y, cle_dtype dt,
                                const cle_loop_state* st, hipStream_t s);
+// Row RMS normalisation of cle_rmsnorm_many (todo micro-batches only with a state).
+cle_status launch_rmsnorm(int n, const void* const* x, void* const* y, int T, int H, float eps,
+                          cle_dtype dt, const cle_loop_state* st, hipStream_t s);
+// Router logits of cle_gate_logits_many (validated by check_gate); with a
+// loop state, w_gate / bias entries are the bases [L, E, H] / [L, E].
+cle_status launch_gate(int n, const void* const* x, const void* const* w_gate,
+                       const float* const* bias, int T, int H, int E, cle_dtype dt, bool packed,
+                       float* const* logits, const cle_loop_state* st, hipStream_t s);
+cle_status check_gate(int T, int H, int E, cle_dtype dt, int32_t w_layout);
 // cle_grouped_expert_ffn with an optional loop state; launch = false only
 // validates the arguments.
 cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, const void* w2,

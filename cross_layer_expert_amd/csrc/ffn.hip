@@ -356,6 +356,7 @@ struct TileArgs {
   int ldo;              // output row stride
   int col;              // this lane's output column in the wavefront's first block
   int nrows;            // valid rows of the tile (1..kTM)
+  const float* bias;    // phase 3: per-column bias added to the float32 output, or NULL
 };
 
 // Instruction order of one half step, for the scheduler: the NB weight
@@ -517,6 +518,11 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
 #pragma unroll
           for (int b = 0; b < HB; ++b)
             o[b * 16] = f32_to_bf16(silu(acc[b][mb][i]) * acc[HB + b][mb][i]);
+        } else if (PHASE == 3) {
+          float* of = reinterpret_cast<float*>(t.out) + row * t.ldo + t.col;
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            of[b * 16] = t.bias ? acc[b][mb][i] + t.bias[t.col + b * 16] : acc[b][mb][i];
         } else {
 #pragma unroll
           for (int b = 0; b < NB; ++b) o[b * 16] = f32_to_bf16(acc[b][mb][i]);
@@ -582,6 +588,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
       t.col = wlo + l16;
     }
     t.ldo = ldo;
+    t.bias = nullptr;
     t.wlo = W + static_cast<int64_t>(wlo) * K;
     t.whi = W + static_cast<int64_t>(whi) * K;
     const int nmb = (t.nrows + 15) / 16;
@@ -640,6 +647,87 @@ __global__ __launch_bounds__(256) void ffn_gemm_f32(const Seg* __restrict__ segs
         static_cast<float*>(sg.y)[static_cast<int64_t>(row) * H + col] = y;
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------- router gate
+// Router logits z = x W_g^T + b of several micro-batches in one launch
+// ("EasyBalance: Cross-Layer Load Balancing in Distributed MoE Inference",
+// §2.1: the routing scores G(h') that top-k selects from).  bf16: the tile
+// engine above as phase 3 (fp32 accumulation and output), one 32-row x
+// (16 * WN * NB)-expert tile per workgroup, K = H in the same fixed order for
+// every tile.  With a loop state, only micro-batches in its todo mask run,
+// each with the weights and bias of its layer l_j.
+constexpr int kGateRows = 32;
+
+struct GateArgs {
+  const uint16_t* x[CLE_MAX_MICROBATCHES];  // [T, H] (float for the f32 path)
+  const uint16_t* wg[CLE_MAX_MICROBATCHES];  // [E, H], or with a loop state the base [L, E, H]
+  const float* bias[CLE_MAX_MICROBATCHES];   // [E] / [L, E], or NULL
+  float* out[CLE_MAX_MICROBATCHES];          // [T, E]
+  const cle_loop_state* st;
+};
+
+__device__ __forceinline__ bool gate_member(const GateArgs& a, int j, const uint16_t*& wg,
+                                            const float*& bias, int64_t wstride, int E) {
+  wg = a.wg[j];
+  bias = a.bias[j];
+  if (a.st) {
+    if (!(a.st->todo >> j & 1)) return false;
+    const int l = a.st->layer[j];
+    wg += static_cast<int64_t>(l) * wstride;
+    if (bias) bias += static_cast<int64_t>(l) * E;
+  }
+  return true;
+}
+
+template <int WN, int NB, bool PACKED>
+__global__ __launch_bounds__(64 * WN, 1) void gate_gemm_bf16(GateArgs a, int T, int H, int E) {
+  constexpr int HB = NB / 2;
+  const int j = blockIdx.y;
+  const uint16_t* wg;
+  const float* bias;
+  if (!gate_member(a, j, wg, bias, static_cast<int64_t>(E) * H, E)) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int ncols = E / (WN * 16 * NB);
+  const int mt = blockIdx.x / ncols, nt = blockIdx.x % ncols;
+  const int row0 = mt * kGateRows;
+  TileArgs t;
+  t.K = H;
+  t.rot = 0;
+  t.nrows = min(kGateRows, T - row0);
+  t.A = a.x[j] + static_cast<int64_t>(row0) * H;
+  t.rmap = nullptr;
+  t.kdiv = 1;
+  const int wlo = (nt * WN + wave) * (16 * NB);
+  t.out = reinterpret_cast<uint16_t*>(a.out[j] + static_cast<int64_t>(row0) * E);
+  t.ldo = E;
+  t.col = wlo + lane % 16;
+  t.bias = bias;
+  t.wlo = wg + static_cast<int64_t>(wlo) * H;
+  t.whi = wg + static_cast<int64_t>(wlo + 16 * HB) * H;
+  if (t.nrows > 16)
+    tile_nmb<3, WN, NB, PACKED, 2>(t, wave, lane);
+  else
+    tile_nmb<3, WN, NB, PACKED, 1>(t, wave, lane);
+}
+
+// f32: one thread per logit, sequential K (the small fp32 shapes).
+__global__ __launch_bounds__(256) void gate_f32(GateArgs a, int T, int H, int E) {
+  const int j = blockIdx.y;
+  const uint16_t* wg16;
+  const float* bias;
+  if (!gate_member(a, j, wg16, bias, static_cast<int64_t>(E) * H * 2, E)) return;
+  const float* x = reinterpret_cast<const float*>(a.x[j]);
+  const float* wg = reinterpret_cast<const float*>(wg16);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+       i < static_cast<int64_t>(T) * E; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = i / E;
+    const int e = static_cast<int>(i % E);
+    float z = 0.f;
+    for (int h = 0; h < H; ++h) z = fmaf(x[t * H + h], wg[static_cast<int64_t>(e) * H + h], z);
+    a.out[j][i] = bias ? z + bias[e] : z;
   }
 }
 
@@ -799,3 +887,68 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
 }
 
 }  // namespace cle
+
+namespace cle {
+
+cle_status launch_gate(int n, const void* const* x, const void* const* wg,
+                       const float* const* bias, int T, int H, int E, cle_dtype dt, bool packed,
+                       float* const* logits, const cle_loop_state* st, hipStream_t s) {
+  if (T == 0) return CLE_OK;
+  GateArgs a;
+  for (int j = 0; j < n; ++j) {
+    a.x[j] = static_cast<const uint16_t*>(x[j]);
+    a.wg[j] = static_cast<const uint16_t*>(wg[j]);
+    a.bias[j] = bias ? bias[j] : nullptr;
+    a.out[j] = logits[j];
+  }
+  a.st = st;
+  if (dt == CLE_F32) {
+    const int64_t blocks = (static_cast<int64_t>(T) * E + 255) / 256;
+    gate_f32<<<dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096), n), dim3(256), 0, s>>>(
+        a, T, H, E);
+    return launch_status();
+  }
+  const unsigned mts = static_cast<unsigned>((T + kGateRows - 1) / kGateRows);
+  if (E % 128 == 0) {
+    const dim3 grid(mts * (E / 128), n);
+    if (packed)
+      gate_gemm_bf16<4, 2, true><<<grid, dim3(256), 0, s>>>(a, T, H, E);
+    else
+      gate_gemm_bf16<4, 2, false><<<grid, dim3(256), 0, s>>>(a, T, H, E);
+  } else {
+    const dim3 grid(mts * (E / 64), n);
+    if (packed)
+      gate_gemm_bf16<2, 2, true><<<grid, dim3(128), 0, s>>>(a, T, H, E);
+    else
+      gate_gemm_bf16<2, 2, false><<<grid, dim3(128), 0, s>>>(a, T, H, E);
+  }
+  return launch_status();
+}
+
+cle_status check_gate(int T, int H, int E, cle_dtype dt, int32_t w_layout) {
+  if (T < 0 || H < 1 || E < 1 || E > CLE_MAX_E) return CLE_EINVAL;
+  if (dt != CLE_BF16 && dt != CLE_F32) return CLE_EINVAL;
+  if (w_layout != CLE_W_ROWMAJOR && !(w_layout == CLE_W_PACKED && dt == CLE_BF16))
+    return CLE_EINVAL;
+  if (dt == CLE_BF16 && (H % 128 || E % 64)) return CLE_EINVAL;
+  return CLE_OK;
+}
+
+}  // namespace cle
+
+extern "C" cle_status cle_gate_logits_many(int32_t n, const void* const* x,
+                                           const void* const* w_gate,
+                                           const float* const* bias, int32_t T, int32_t H,
+                                           int32_t E, cle_dtype dt, int32_t w_layout,
+                                           float* const* logits, void* stream) {
+  using namespace cle;
+  if (n < 1 || n > CLE_MAX_MICROBATCHES || !x || !w_gate || !logits) return CLE_EINVAL;
+  const cle_status c = check_gate(T, H, E, dt, w_layout);
+  if (c != CLE_OK) return c;
+  for (int j = 0; j < n; ++j) {
+    if (!x[j] || !w_gate[j] || !logits[j]) return CLE_EINVAL;
+    if (!aligned(x[j], 16) || !aligned(w_gate[j], 16) || !aligned(logits[j], 4)) return CLE_EINVAL;
+  }
+  return launch_gate(n, x, w_gate, bias, T, H, E, dt, w_layout == CLE_W_PACKED, logits, nullptr,
+                     as_stream(stream));
+}

@@ -433,14 +433,24 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
   if (d->log && d->log_cap < 1) return CLE_EINVAL;
   const int64_t A = static_cast<int64_t>(T) * k;
   if (A > INT32_MAX) return CLE_EUNSUPPORTED;
+  const bool gated = d->w_gate != nullptr;
+  if (d->prenorm != 0 && d->prenorm != 1) return CLE_EINVAL;
+  if (d->prenorm && !(d->norm_eps >= 0.0f)) return CLE_EINVAL;
+  if (gated) {
+    const cle_status c = check_gate(T, H, E, static_cast<cle_dtype>(d->dtype), d->w_layout);
+    if (c != CLE_OK) return c;
+    if (!aligned(d->w_gate, 16)) return CLE_EINVAL;
+  }
   for (int j = 0; j < n; ++j) {
-    if (!d->logits[j] || !d->h[j] || !d->idx[j] || !d->gate[j] || !d->counts[j] ||
+    if (gated ? !d->gate_logits[j] : !d->logits[j]) return CLE_EINVAL;
+    if (!d->h[j] || !d->idx[j] || !d->gate[j] || !d->counts[j] ||
         !d->offsets[j] || !d->dest[j] || !d->src[j] || !d->act[j] || !d->yp[j])
       return CLE_EINVAL;
     if (!aligned(d->h[j], 16) || !aligned(d->yp[j], 16)) return CLE_EINVAL;
     if (ns > 0 && (!d->act_shared[j] || !d->y_shared[j] || !aligned(d->y_shared[j], 16)))
       return CLE_EINVAL;
     if (d->restart && (!d->h0[j] || !aligned(d->h0[j], 16))) return CLE_EINVAL;
+    if (d->prenorm && (!d->xn[j] || !aligned(d->xn[j], 16))) return CLE_EINVAL;
   }
   const size_t need = cle_workspace_bytes(CLE_OP_DISPATCH_MANY, T, E, k, 0, n);
   if (!d->ws_dispatch || d->ws_dispatch_bytes < need || !aligned(d->ws_dispatch, 256))
@@ -454,11 +464,12 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
     q.xp = nullptr;
     q.act = d->act[j];
     q.yp = d->yp[j];
+    const void* xin = d->prenorm ? d->xn[j] : d->h[j];  // what the experts read
     q.shared_rows = ns > 0 ? T : 0;
-    q.x_shared = ns > 0 ? d->h[j] : nullptr;
+    q.x_shared = ns > 0 ? xin : nullptr;
     q.act_shared = ns > 0 ? d->act_shared[j] : nullptr;
     q.y_shared = ns > 0 ? d->y_shared[j] : nullptr;
-    q.x = d->h[j];
+    q.x = xin;
     q.src = d->src[j];
     q.k = k;
   }
@@ -470,7 +481,29 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
 
   hipStream_t s = as_stream(stream);
   const cle_loop_state* st = d->state;
-  rc = launch_route(n, d->logits, T, E, k, d->idx, d->gate, st, static_cast<int64_t>(T) * E, s);
+  if (d->prenorm) {
+    const void* hs[CLE_MAX_MICROBATCHES];
+    for (int j = 0; j < n; ++j) hs[j] = d->h[j];
+    rc = launch_rmsnorm(n, hs, d->xn, T, H, d->norm_eps, dt, st, s);
+    if (rc != CLE_OK) return rc;
+  }
+  if (gated) {
+    const void* xs[CLE_MAX_MICROBATCHES];
+    const void* wgs[CLE_MAX_MICROBATCHES];
+    const float* bs[CLE_MAX_MICROBATCHES];
+    for (int j = 0; j < n; ++j) {
+      xs[j] = d->prenorm ? d->xn[j] : d->h[j];
+      wgs[j] = d->w_gate;
+      bs[j] = d->gate_bias;
+    }
+    rc = launch_gate(n, xs, wgs, bs, T, H, E, dt, d->w_layout == CLE_W_PACKED, d->gate_logits, st,
+                     s);
+    if (rc != CLE_OK) return rc;
+    rc = launch_route(n, const_cast<const float* const*>(d->gate_logits), T, E, k, d->idx,
+                      d->gate, st, 0, s);
+  } else {
+    rc = launch_route(n, d->logits, T, E, k, d->idx, d->gate, st, static_cast<int64_t>(T) * E, s);
+  }
   if (rc != CLE_OK) return rc;
   rc = launch_dispatch_many(n, d->idx, T, k, E, d->counts, d->offsets, d->dest, d->src,
                             d->ws_dispatch, st, s);

@@ -21,7 +21,8 @@ import torch
 
 from . import (BF16, LOOP_STATE_BYTES, OP_DISPATCH, OP_DISPATCH_MANY, OP_FFN, W_PACKED,
                W_ROWMAJOR, LoopDesc, combine, combine_many, dispatch, dispatch_many,
-               grouped_expert_ffn, ids_of, loop_init, loop_step, make_desc, mask_of,
+               NORM_EPS, gate_logits_many, grouped_expert_ffn, ids_of, loop_init, loop_step,
+               make_desc, mask_of, rmsnorm_many,
                read_loop_state, route, route_many, schedule_step_raw, workload_stats,
                workspace_bytes)
 
@@ -31,18 +32,27 @@ class Engine:
 
     weights: (w13 [L,E,2I,H], w2 [L,E,H,I], w13_shared | None, w2_shared | None),
     row-major, or all four packed by pack_weights (then packed=True),
-    logits: tensor [n, L, T, E] float32 on the device, h0: tensor [n, T, H].
+    logits: tensor [n, L, T, E] float32 on the device, or None with `gate`;
+    h0: tensor [n, T, H];
+    gate: None, or (w_gate [L, E, H], bias [L, E] float32 | None): routing
+    from the hidden state through the linear router of each layer instead of
+    the given logits (w_gate packed too when packed=True).
+    prenorm: the router and the experts read the RMS-normalised rows of h
+    (kept in xn), the combine adds to h itself (a pre-norm block).
     """
 
     def __init__(self, weights, logits, h0, D, k, policy, m, start_layers=None, stream=None,
                  fused_gather=True, batched=True, packed=False, device_loop=False, restart=False,
-                 log_cap=4096):
+                 log_cap=4096, gate=None, prenorm=False):
         self.w13, self.w2, self.w13s, self.w2s = weights
         self.packed = packed  # the weights were written by pack_weights (bf16)
         self.L, self.E, I2, self.H = self.w13.shape
         self.I = I2 // 2
         self.ns = 0 if self.w13s is None else self.w13s.shape[1]
         self.logits = logits
+        self.wg, self.gbias = gate if gate is not None else (None, None)
+        if logits is None and self.wg is None:
+            raise ValueError("either router logits or a router (gate) is needed")
         self.n, self.T = h0.shape[0], h0.shape[1]
         self.k, self.D, self.policy, self.m = k, D, int(policy), m
         self.start = list(start_layers) if start_layers else [0] * self.n
@@ -52,6 +62,9 @@ class Engine:
         i32 = dict(dtype=torch.int32, device=dev)
         self.h0 = h0
         self.h = h0.clone()
+        self.prenorm = bool(prenorm)
+        self.xn = torch.empty_like(self.h) if self.prenorm else None
+        self.xin = self.xn if self.prenorm else self.h  # what the router and experts read
         self.idx = torch.empty((n, T, k), **i32)
         self.gates = torch.empty((n, T, k), dtype=torch.float32, device=dev)
         self.counts = torch.zeros((n, E), **i32)
@@ -72,6 +85,8 @@ class Engine:
             self.y_sh = torch.empty((n, self.ns, T, H), dtype=dt, device=dev)
         else:
             self.act_sh = self.y_sh = None
+        self.glog = (torch.empty((n, T, E), dtype=torch.float32, device=dev)
+                     if self.wg is not None else None)
         self.w_dev = torch.zeros((n, D), **i32)
         self.acc = torch.zeros(4, dtype=torch.int64, device=dev)
         self.w_host = torch.zeros((n, D), dtype=torch.int32).pin_memory()
@@ -103,8 +118,14 @@ class Engine:
         d.dtype = 0 if self.h.dtype == torch.bfloat16 else 1
         d.w_layout = W_PACKED if self.packed else W_ROWMAJOR
         d.restart = 1 if self.restart else 0
+        if self.wg is not None:
+            d.w_gate = self.wg.data_ptr()
+            d.gate_bias = None if self.gbias is None else self.gbias.data_ptr()
         for j in range(self.n):
-            d.logits[j] = self.logits[j].data_ptr()
+            if self.wg is not None:
+                d.gate_logits[j] = self.glog[j].data_ptr()
+            else:
+                d.logits[j] = self.logits[j].data_ptr()
             d.h[j] = self.h[j].data_ptr()
             d.h0[j] = self.h0[j].data_ptr()
             d.idx[j] = self.idx[j].data_ptr()
@@ -129,18 +150,22 @@ class Engine:
         d.log = self.log.data_ptr()
         d.log_cap = self.log.numel()
         d.state = self.state.data_ptr()
+        if self.prenorm:
+            d.prenorm, d.norm_eps = 1, NORM_EPS
+            for j in range(self.n):
+                d.xn[j] = self.xn[j].data_ptr()
         return d
 
     def _desc(self, j):
         if self.fused:
             d = make_desc(0, self.T * self.k, self.offsets[j], None, self.act[j], self.yp[j],
-                          x=self.h[j], src=self.src[j], k=self.k)
+                          x=self.xin[j], src=self.src[j], k=self.k)
         else:
             d = make_desc(0, self.T * self.k, self.offsets[j], self.xp[j], self.act[j],
                           self.yp[j])
         if self.ns:
             d.shared_rows = self.T
-            d.x_shared = self.h[j].data_ptr()
+            d.x_shared = self.xin[j].data_ptr()
             d.act_shared = self.act_sh[j].data_ptr()
             d.y_shared = self.y_sh[j].data_ptr()
         return d
@@ -185,11 +210,24 @@ class Engine:
         return st
 
     # ------------------------------------------------------------ one step
+    def _scores(self, js):
+        """Router logits of the micro-batches js at their current layers: the
+        given ones, or from h through each layer's router (one launch)."""
+        if self.prenorm:
+            rmsnorm_many([self.h[j] for j in js], [self.xn[j] for j in js], stream=self.stream)
+        if self.wg is None:
+            return [self.logits[j, self.l[j]] for j in js]
+        out = [self.glog[j] for j in js]
+        bias = None if self.gbias is None else [self.gbias[self.l[j]] for j in js]
+        gate_logits_many([self.xin[j] for j in js], [self.wg[self.l[j]] for j in js], out,
+                         bias=bias, packed=self.packed, stream=self.stream)
+        return out
+
     def route_dispatch(self, j):
         """AttnRouteDispatch for micro-batch j at its current layer."""
         s = self.stream
-        route(self.logits[j, self.l[j]], self.k, self.idx[j], self.gates[j], stream=s)
-        dispatch(self.idx[j], self.E, self.h[j], self.counts[j], self.offsets[j], self.dest[j],
+        route(self._scores([j])[0], self.k, self.idx[j], self.gates[j], stream=s)
+        dispatch(self.idx[j], self.E, self.xin[j], self.counts[j], self.offsets[j], self.dest[j],
                  self.src[j], None if self.fused else self.xp[j], self.ws_dispatch, stream=s)
 
     def route_dispatch_many(self, js):
@@ -197,8 +235,7 @@ class Engine:
         one launch per pass."""
         s = self.stream
         idx = [self.idx[j] for j in js]
-        route_many([self.logits[j, self.l[j]] for j in js], self.k, idx,
-                   [self.gates[j] for j in js], stream=s)
+        route_many(self._scores(js), self.k, idx, [self.gates[j] for j in js], stream=s)
         dispatch_many(idx, self.E, [self.counts[j] for j in js], [self.offsets[j] for j in js],
                       [self.dest[j] for j in js], [self.src[j] for j in js], self.ws_dispatch,
                       stream=s)

@@ -248,6 +248,42 @@ cle_status cle_combine_many(int32_t n, const void* const* yp, const int32_t* con
                             void* stream);
 
 /*
+ * cle_rmsnorm_many -- the MoE block's normalised input, for n micro-batches in
+ * one launch: y[t] = x[t] / sqrt(mean_h x[t][h]^2 + eps).
+ * Paper §2.1: the MoE of layer l takes the post-attention state h'_l and its
+ * output is added back to it; the experts (and the router) read the
+ * unit-weight RMS-normalised rows while the residual keeps h'_l.
+ *   x, y  HOST arrays of n pointers to [T, H] (dt); y may alias x.
+ * The sum of squares is taken in float32 in a fixed order and the row is
+ * rounded once to dt (bitwise reproducible).
+ * Requires 1 <= n <= CLE_MAX_MICROBATCHES, T >= 0, H % 8 == 0, eps >= 0.
+ */
+cle_status cle_rmsnorm_many(int32_t n, const void* const* x, void* const* y, int32_t T,
+                            int32_t H, float eps, cle_dtype dt, void* stream);
+
+/*
+ * cle_gate_logits_many -- router logits from the hidden states, for n
+ * micro-batches in one launch: z_j = x_j W_g,j^T + b_j.
+ * Paper §2.1: the routing scores G(h'_l) that top-k selects from, with G a
+ * linear router (no activation); the optional per-expert bias is a fixed
+ * offset of each expert's score.  Route the result with cle_route_many.
+ *   x       HOST array of n pointers to [T, H] (dt) hidden states.
+ *   w_gate  HOST array of n pointers to [E, H] (dt) router weights (each
+ *           micro-batch's own layer), row-major or packed (see
+ *           cle_pack_weights; bf16 only).
+ *   bias    NULL, or HOST array of n pointers to [E] float32 (entries may be NULL).
+ *   logits  HOST array of n pointers to [T, E] float32 out.
+ * bf16: products of bf16 values summed in float32 over H in one fixed order
+ * (results are bitwise reproducible); f32: float32 throughout.
+ * Requires 1 <= n <= CLE_MAX_MICROBATCHES, 1 <= E <= CLE_MAX_E, T >= 0
+ * (T == 0 enqueues nothing); bf16: H % 128 == 0, E % 64 == 0.
+ */
+cle_status cle_gate_logits_many(int32_t n, const void* const* x, const void* const* w_gate,
+                                const float* const* bias, int32_t T, int32_t H, int32_t E,
+                                cle_dtype dt, int32_t w_layout, float* const* logits,
+                                void* stream);
+
+/*
  * cle_workload_stats -- per-group workloads and their step statistics.
  * Paper §2.3, Eq. (2) and Eq. (3); the even expert-device mapping (Figure 1)
  * gives group d the experts [d*E/D, (d+1)*E/D).
@@ -377,11 +413,26 @@ typedef struct {
                                        s % log_cap */
   int64_t log_cap;
   cle_loop_state* state;
+  /* Routing from the hidden state (optional): when w_gate is not NULL, the
+   * router logits of micro-batch j at layer l are computed from h_j by
+   * cle_gate_logits_many (weights w_gate[l], bias gate_bias[l]) into
+   * gate_logits[j], and `logits` is not read. */
+  const void* w_gate;               /* [L, E, H] (dtype, w_layout) or NULL */
+  const float* gate_bias;           /* [L, E] float32 or NULL */
+  float* gate_logits[64];           /* [T, E] float32 scratch (w_gate only) */
+  /* Normalised MoE input (optional): with prenorm = 1 each routed micro-batch's
+   * rows are first RMS-normalised (cle_rmsnorm_many, norm_eps) into xn[j];
+   * the router and the experts read xn[j], the combine adds to h[j]. */
+  int32_t prenorm;
+  float norm_eps;
+  void* xn[64];                     /* [T, H] (prenorm only) */
 } cle_loop_desc;
 
 /*
  * cle_loop_step -- enqueue one iteration of Algorithm 1 on `stream`:
- *   1. route and dispatch the micro-batches in state->todo, each at its l_j;
+ *   1. route and dispatch the micro-batches in state->todo, each at its l_j
+ *      (from logits[j] at layer l_j, or with w_gate from h_j -- xn_j with
+ *      prenorm -- through the router of layer l_j);
  *   2. on the device: w[j][d] for j in S, RunSet = Schedule(S, m) as in
  *      cle_schedule_step, acc as in cle_workload_stats, the log entry,
  *      run_layer = l_j and l_j += 1 for the members, S and todo updated

@@ -23,7 +23,8 @@ counting sort, workloads, schedules) is exact.  Utilisation is an exact
 
 Pinning status of every function is listed in each module's header.
 """
-from .moe import route, dispatch, swiglu_expert, expert_ffn, combine, widen  # noqa: F401
+from .moe import (route, dispatch, swiglu_expert, expert_ffn, combine, widen,  # noqa: F401
+                  gate_logits, rmsnorm)
 from .balance import (group_workload, effective_workload, utilization, step_stats,  # noqa: F401
                       util_of, schedule, same_peak_windows, POLICIES)
 from .engine import run_schedule_only, run_engine, moe_layer  # noqa: F401

@@ -17,21 +17,24 @@ from . import moe
 from .balance import group_workload, schedule, step_stats, utilization, combined
 
 
-def moe_layer(h, logits, k, w13_l, w2_l, w13s_l=None, w2s_l=None):
+def moe_layer(h, logits, k, w13_l, w2_l, w13s_l=None, w2s_l=None, prenorm=False,
+              eps=1e-6):
     """One MoE layer on hidden rows h (float64 [T, H]).
 
     [PAPER] §2.1 with attention taken as the identity (h' = h):
         route -> dispatch -> experts -> Eq. (1) combine -> residual.
+    prenorm: the experts read rmsnorm(h), the residual is h itself.
     Returns a dict with every intermediate (float64 for values).
     """
     E = w13_l.shape[0]
+    xin = moe.rmsnorm(h, eps) if prenorm else h
     idx, gates = moe.route(logits, k)
     counts, offsets, dest, src = moe.dispatch(idx, E)
-    xp = moe.permute_rows(h, src, k)
+    xp = moe.permute_rows(xin, src, k)
     yp = moe.expert_ffn(xp, offsets, w13_l, w2_l)
     ysh = None
     if w13s_l is not None and len(w13s_l):
-        ysh = [moe.swiglu_expert(h, w13s_l[s], w2s_l[s]) for s in range(len(w13s_l))]
+        ysh = [moe.swiglu_expert(xin, w13s_l[s], w2s_l[s]) for s in range(len(w13s_l))]
     y = moe.combine(yp, dest, gates, k, y_shared=ysh, residual=h)
     return dict(idx=idx, gates=gates, counts=counts, offsets=offsets, dest=dest, src=src,
                 xp=xp, yp=yp, y_shared=ysh, y=y)

@@ -11,6 +11,10 @@ Pins (tests/test_oracle_moe.py):
 * expert_ffn -- one expert holding every token equals the dense SwiGLU MLP.
 * combine    -- Yp = Xp gives Y = X * sum(gates); a hand-worked example;
                 shared-expert and residual terms.
+* rmsnorm    -- a hand-worked row ([3, 4]); constant rows give +-1; outputs
+                have unit mean square; positive scaling leaves them unchanged.
+* gate_logits -- one-hot router rows pick hidden columns (closed form); zero
+                weights leave the bias; relabelling experts permutes columns.
 """
 from __future__ import annotations
 
@@ -26,6 +30,29 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+def rmsnorm(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """The MoE block's normalised input rows: h / sqrt(mean(h^2) + eps).
+
+    [PAPER] §2.1 writes the layer as h_{l+1} = h'_l + MLP(h'_l); reading: the
+    experts and the router read the RMS-normalised rows of h'_l (unit weight,
+    as in pre-norm transformer blocks) while the residual keeps h'_l."""
+    h = np.asarray(h, dtype=np.float64)
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+
+
+def gate_logits(h: np.ndarray, w_gate: np.ndarray, bias=None) -> np.ndarray:
+    """Router scores of the tokens h [T, H] (float64): z = h W_g^T + b, [T, E].
+
+    [PAPER] §2.1: top-k selects from G(h'_l); G is taken as a linear router
+    with weights W_g [E, H] (row e scores expert e) and an optional fixed
+    per-expert offset b [E] (the synthetic skew; reading R2's bias).
+    Evaluated in float64 on the exact values of the stored weights."""
+    z = np.asarray(h, dtype=np.float64) @ np.asarray(w_gate, dtype=np.float64).T
+    if bias is not None:
+        z = z + np.asarray(bias, dtype=np.float64)[None, :]
+    return z
 
 
 def route(logits: np.ndarray, k: int):

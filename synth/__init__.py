@@ -34,6 +34,7 @@ _FAM_LOGIT = 2
 _FAM_HIDDEN = 3
 _FAM_WEIGHT = 4
 _FAM_BIAS = 5
+_FAM_GATE = 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -203,3 +204,34 @@ def weights_torch(cfg: Config, seed: int, device, layers: int | None = None):
     else:
         w13s = w2s = None
     return w13, w2, w13s, w2s
+
+
+# ---------------------------------------------------------------- router weights
+# Routing from the hidden state: z = h W_g^T + b.  W_g ~ N(0, 1/sqrt(H)) so that
+# h W_g^T of an N(0, 1) hidden row is about N(0, 1) -- the noise part of the
+# given-logits recipe -- and b is that recipe's per-layer expert bias (profile
+# 0), so routing from h has the same skew structure.
+def gate_bias(cfg: Config, seed: int) -> np.ndarray:
+    """Per-layer expert bias of the router, float32 [L, E]."""
+    return np.stack([expert_bias(cfg, seed, 0, l) for l in range(cfg.L)]).astype(np.float32)
+
+
+def gate_weights_numpy(cfg: Config, seed: int) -> np.ndarray:
+    """Router weights [L, E, H] in storage form (small configs)."""
+    r = _rng(seed, _FAM_GATE, 0, 0)
+    w = r.normal(0.0, 1.0 / np.sqrt(cfg.H), (cfg.L, cfg.E, cfg.H)).astype(np.float32)
+    return store(w, cfg.dtype)
+
+
+def gate_weights_torch(cfg: Config, seed: int, device):
+    """Router weights [L, E, H] drawn on ``device`` with a seeded generator."""
+    import torch
+
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + 29)
+    out = torch.empty((cfg.L, cfg.E, cfg.H), dtype=tdt, device=device)
+    for l in range(cfg.L):
+        tmp = torch.randn((cfg.E, cfg.H), generator=g, device=device, dtype=torch.float32)
+        out[l].copy_(tmp.mul_(1.0 / float(np.sqrt(cfg.H))))
+    return out

@@ -258,6 +258,9 @@ def test_loop_calls_validate_on_host():
     assert step(desc(m=3)) == cle.EINVAL                      # m > n
     assert step(desc(policy=7)) == cle.EINVAL
     assert step(desc(restart=2)) == cle.EINVAL
+    assert step(desc(prenorm=2)) == cle.EINVAL
+    assert step(desc(prenorm=1, norm_eps=1e-6)) == cle.EINVAL   # xn entries missing
+    assert step(desc(w_gate=1 << 26, E=96, D=4)) == cle.EINVAL  # gate: E % 64 (bf16)
     assert step(desc(I=96)) == cle.EINVAL                     # I % 64 (expert launch)
     assert step(desc(state=None)) == cle.EINVAL
     assert step(desc(ws_dispatch_bytes=0)) == cle.EWORKSPACE
@@ -278,3 +281,44 @@ def test_loop_calls_validate_on_host():
     assert S(256, 2, 2, 4, 1, 2, 256, None) == cle.EINVAL     # bit beyond n
     assert S(256, 2, 2, 3, 3, 2, 256, None) == cle.EINVAL     # m > n
     assert S(256, 21, 2, (1 << 21) - 1, 1, 3, 256, None) == cle.EUNSUPPORTED
+
+
+def test_gate_logits_validate_on_host():
+    """cle_gate_logits_many(n, x, w_gate, bias, T, H, E, dt, w_layout, logits, stream)."""
+    import ctypes
+    L = cle._lib
+    vp = ctypes.c_void_p
+
+    def arr(*v):
+        return (vp * len(v))(*v)
+
+    one = arr(256)
+    G = L.cle_gate_logits_many
+    assert G(0, one, one, None, 16, 128, 64, cle.BF16, 0, one, None) == cle.EINVAL    # n < 1
+    assert G(65, one, one, None, 16, 128, 64, cle.BF16, 0, one, None) == cle.EINVAL   # n > 64
+    assert G(1, None, one, None, 16, 128, 64, cle.BF16, 0, one, None) == cle.EINVAL   # no x
+    assert G(1, arr(None), one, None, 16, 128, 64, cle.BF16, 0, one, None) == cle.EINVAL
+    assert G(1, one, one, None, 16, 96, 64, cle.BF16, 0, one, None) == cle.EINVAL     # H % 128
+    assert G(1, one, one, None, 16, 128, 96, cle.BF16, 0, one, None) == cle.EINVAL    # E % 64
+    assert G(1, one, one, None, 16, 128, 2048, cle.BF16, 0, one, None) == cle.EINVAL  # E > max
+    assert G(1, one, one, None, 16, 64, 8, cle.F32, cle.W_PACKED, one, None) == cle.EINVAL
+    assert G(1, one, one, None, -1, 128, 64, cle.BF16, 0, one, None) == cle.EINVAL    # T < 0
+    assert G(1, one, arr(8), None, 16, 128, 64, cle.BF16, 0, one, None) == cle.EINVAL  # unaligned
+    assert G(1, one, one, None, 16, 128, 64, 7, 0, one, None) == cle.EINVAL           # dtype
+
+
+def test_rmsnorm_and_prenorm_validate_on_host():
+    import ctypes
+    L = cle._lib
+    vp = ctypes.c_void_p
+    one = (vp * 1)(256)
+    N = L.cle_rmsnorm_many
+    assert N(0, one, one, 4, 64, 1e-6, cle.BF16, None) == cle.EINVAL      # n < 1
+    assert N(1, None, one, 4, 64, 1e-6, cle.BF16, None) == cle.EINVAL     # no x
+    assert N(1, one, (vp * 1)(None), 4, 64, 1e-6, cle.BF16, None) == cle.EINVAL
+    assert N(1, one, one, 4, 60, 1e-6, cle.BF16, None) == cle.EINVAL      # H % 8
+    assert N(1, one, one, -1, 64, 1e-6, cle.BF16, None) == cle.EINVAL     # T < 0
+    assert N(1, one, one, 4, 64, -1.0, cle.BF16, None) == cle.EINVAL      # eps < 0
+    assert N(1, one, one, 4, 64, float("nan"), cle.BF16, None) == cle.EINVAL
+    assert N(1, (vp * 1)(8), one, 4, 64, 1e-6, cle.BF16, None) == cle.EINVAL  # unaligned
+    assert N(1, one, one, 0, 64, 1e-6, cle.BF16, None) == cle.OK          # T == 0: nothing

@@ -160,3 +160,46 @@ def test_widen_bf16_exact():
     v = oracle.widen(bits, "bf16")
     assert v[0] == 1.0 and v[1] == -1.0 and v[2] == 3.140625 and v[3] == 0.0
     assert math.copysign(1.0, v[4]) == -1.0 and math.isinf(v[5])
+
+
+def test_gate_logits_special_cases():
+    """Router scores: one-hot router rows pick hidden columns plus the bias
+    (a closed form); zero weights leave only the bias, so routing follows
+    the bias ranking; relabelling the experts permutes the score columns."""
+    rng = np.random.default_rng(4)
+    T, H, E = 7, 12, 5
+    h = rng.standard_normal((T, H))
+    cols = [3, 0, 11, 3, 7]
+    w = np.zeros((E, H))
+    for e, c in enumerate(cols):
+        w[e, c] = 1.0
+    b = np.array([0.5, -1.0, 0.0, 2.0, 0.25])
+    z = oracle.gate_logits(h, w, b)
+    for t in range(T):
+        for e, c in enumerate(cols):
+            assert z[t, e] == h[t, c] + b[e]
+    z0 = oracle.gate_logits(h, np.zeros((E, H)), b)
+    assert np.array_equal(z0, np.broadcast_to(b, (T, E)))
+    idx, _ = oracle.route(z0.astype(np.float32), 2)
+    assert (idx == [3, 0]).all()                     # the two largest biases, every token
+    wr = rng.standard_normal((E, H))
+    perm = rng.permutation(E)
+    assert np.allclose(oracle.gate_logits(h, wr[perm], b[perm]),
+                       oracle.gate_logits(h, wr, b)[:, perm], rtol=0, atol=1e-12)
+    assert oracle.gate_logits(h, w).shape == (T, E)   # no bias
+
+
+def test_rmsnorm_closed_forms():
+    """[3, 4] has mean square 12.5, so it maps to [3, 4] / sqrt(12.5); a
+    constant row maps to +-1 (eps = 0); outputs have unit mean square and do
+    not change when the row is scaled by a positive factor."""
+    y = oracle.rmsnorm(np.array([[3.0, 4.0]]), eps=0.0)
+    assert np.allclose(y, [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=0, atol=1e-15)
+    assert np.array_equal(oracle.rmsnorm(np.full((2, 6), -2.5), eps=0.0), -np.ones((2, 6)))
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 64)) * rng.uniform(0.1, 10, (5, 1))
+    y = oracle.rmsnorm(x, eps=0.0)
+    assert np.allclose(np.mean(y * y, axis=1), 1.0, rtol=0, atol=1e-12)
+    assert np.allclose(oracle.rmsnorm(7.5 * x, eps=0.0), y, rtol=0, atol=1e-12)
+    # eps damps only rows of tiny scale
+    assert np.allclose(oracle.rmsnorm(x, eps=1e-6), y, rtol=1e-5, atol=0)
