@@ -279,15 +279,21 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 
 // Grouped GEMM tile kernel (bf16, gfx950).
 //
-// A tile is 128 rows x (WN * NB) weight blocks of 16 rows.  Wavefront w owns
-// NB consecutive weight blocks -- phase 1: NB/2 blocks of gate rows and the
-// NB/2 blocks of up rows of the same act columns, so the SwiGLU epilogue is
-// local; phase 2: NB blocks of output columns -- and computes all 128 rows of
-// them.  The standard tile is WN = 8 wavefronts x NB = 2 blocks (128 act
-// columns / 256 output columns); shapes that do not divide into it use
-// WN = 4 x NB = 2.  (Four wavefronts x four blocks reads 40 % fewer operand
-// bytes from LDS per stage but measured slower: with one wavefront per SIMD
-// the memory and barrier stalls of a stage are not hidden.)
+// A tile is 128 rows x (WN * NB) weight blocks of 16 rows.  Wavefront w
+// loads NB consecutive weight blocks -- phase 1: NB/2 blocks of gate rows and
+// the NB/2 blocks of up rows of the same act columns; phase 2: NB blocks of
+// output columns -- and 128/WN rows of A per stage.  For the MFMAs the
+// standard 8-wavefront tile (NB = 2: 128 act columns / 256 output columns) is
+// split 2 x 4: wavefront (rg, cg) computes rows 64*rg .. 64*rg+63 of the four
+// blocks loaded by wavefronts 2cg and 2cg+1 (gate/up pairs stay together, so
+// the SwiGLU epilogue is local).  Per K slice a wavefront then reads 4 A and
+// 4 weight fragments from LDS instead of 8 + 2, which takes a fifth off the
+// LDS reads that compete with the direct loads for the LDS port (measured
+// together with the exact K-loop tail below:
+// gate/up unchanged on the Qwen3 step, down 4 % and long-prefill phases 5-7 %
+// faster).  Shapes that do not divide into it use WN = 4 x NB = 2, one row
+// group.  (Four wavefronts x four blocks, one wavefront per SIMD, measured
+// slower: the memory and barrier stalls of a stage are not hidden.)
 //
 //  * Operands move with direct global->LDS loads (global_load_lds_dwordx4, no
 //    registers) into a ring of kStages LDS stages, two stages in flight.
@@ -378,13 +384,27 @@ __device__ __forceinline__ void half_step_order() {
   mfma_read_pairs<0, NMB, NB>();
 }
 
-// The K loop and epilogue of one tile computing NMB 16-row blocks (a
-// compile-time count, so the MFMA sequence has no data-dependent branches).
-template <int PHASE, int WN, int NB, bool PACKED, int NMB>
+// The K loop and epilogue of one tile.  Loading and computing are split
+// differently: wavefront w loads weight blocks w*NB .. w*NB+NB-1 and A row
+// blocks w*XB .. w*XB+XB-1 of every stage, while for the MFMAs the WN
+// wavefronts form RH row groups x WN/RH column groups.  Wavefront (rh, cg)
+// computes rows rh*128/RH .. +128/RH of weight blocks cg*RB .. cg*RB+RB-1
+// (RB = NB*RH; those are the blocks loaded by wavefronts cg*RH .. cg*RH+RH-1).
+// RH = 2 reads 4 A + 4 weight fragments per K slice where RH = 1 reads 8 + 2,
+// a fifth fewer LDS operand bytes per stage, with the same loads and MFMAs.
+// RG is this wavefront's row group and NMB the number of 16-row blocks it
+// computes (0 .. 8/RH); both are compile-time values, so the MFMA sequence
+// has no data-dependent branches and every LDS operand offset is a constant.
+template <int PHASE, int WN, int NB, bool PACKED, int RH, int RG, int NMB>
 __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) {
-  static_assert(WN * NB <= kBlocks, "weight blocks per tile");
+  static_assert(WN * NB <= kBlocks && WN % RH == 0 && kMB % RH == 0, "weight blocks per tile");
+  static_assert(NMB >= 0 && NMB <= kMB / RH && RG >= 0 && RG < RH, "row blocks per wavefront");
   constexpr int XB = kMB / WN;  // A row blocks loaded by each wavefront
   constexpr int HB = NB / 2;
+  constexpr int RB = NB * RH;   // weight blocks each wavefront computes
+  constexpr int AM = NMB > 0 ? NMB : 1;
+  const int cg = wave % (WN / RH);
+  constexpr int xb0 = RG * (kMB / RH);  // first A row block of this wavefront
   const int KT = t.K / kKS;
   // load side: this lane fetches row lr of each 8-row group, chunk lc
   const int lr = lane / 8, lc = (lane % 8) ^ (lane / 8);
@@ -411,11 +431,11 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   const int pos0 = r8 * 8 + ((0 + lane / 16) ^ r8);
   const int pos1 = r8 * 8 + ((4 + lane / 16) ^ r8);
 
-  f32x4 acc[NB][NMB];
+  f32x4 acc[RB][AM];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int b = 0; b < RB; ++b)
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[b][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < AM; ++mb) acc[b][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // request K stage KT_ (of the rotated order) into ST
 #define CLE_ISSUE(ST, KT_)                                                          \
@@ -430,53 +450,63 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
       _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
         dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
   }
-  // The operands of one K slice of a stage: NB weight fragments and NMB A
+  // The operands of one K slice of a stage: RB weight fragments and NMB A
   // fragments, read from LDS into registers.  Slice 0 and slice 1 have their
-  // own registers.
-  bf16x8 fb[2][NB], fa[2][NMB];
+  // own registers.  A wavefront with no row blocks reads and computes nothing.
+  bf16x8 fb[2][RB], fa[2][AM];
 #define CLE_READ(ST, H)                                                             \
-  {                                                                                 \
+  if constexpr (NMB > 0) {                                                          \
     const int pos = (H) == 0 ? pos0 : pos1;                                         \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
-      fb[H][b] = __builtin_bit_cast(bf16x8, ST.w[wave * NB + b][rg][pos]);          \
+    _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
+      fb[H][b] = __builtin_bit_cast(bf16x8, ST.w[cg * RB + b][rg][pos]);            \
     _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                              \
-      fa[H][mb] = __builtin_bit_cast(bf16x8, ST.x[mb][rg][pos]);                    \
+      fa[H][mb] = __builtin_bit_cast(bf16x8, ST.x[xb0 + mb][rg][pos]);              \
   }
 #define CLE_MFMA(H)                                                                 \
   _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                                \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
+    _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
       acc[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[H][mb], fb[H][b], acc[b][mb], 0, 0, 0);
   // Software pipeline by half a stage.  On entry to step KT_ the slice-0
   // MFMAs of stage KT_ are issued and its slice-1 operands are in registers;
   // stage KT_ sits in buffer CUR and stage KT_+1 in NXT.  The step waits for
-  // this wavefront's loads of stage KT_+1 (stage KT_+2 may stay in flight),
-  // synchronises (every wavefront's loads of KT_+1 have landed, and every
-  // wavefront has finished reading CUR), requests stage KT_+3 into CUR, then
-  // issues the slice-1 MFMAs of KT_ while reading slice 0 of KT_+1, and the
-  // slice-0 MFMAs of KT_+1 while reading its slice 1, so the LDS reads of a
-  // stage overlap the MFMAs of its neighbours.  Requests are unconditional
-  // (the stage index is clamped at the end, re-reading the last stage into a
-  // finished buffer) so that every wavefront always has exactly kPerStep
-  // requests per stage in flight and the compiler can tell which buffer each
-  // request writes.
+  // this wavefront's loads of stage KT_+1 (W = the loads it may leave in
+  // flight: stage KT_+2 if that exists), synchronises (every wavefront's
+  // loads of KT_+1 have landed, and every wavefront has finished reading
+  // CUR), requests stage KT_+3 into CUR if that exists, then issues the
+  // slice-1 MFMAs of KT_ while reading slice 0 of KT_+1, and the slice-0
+  // MFMAs of KT_+1 while reading its slice 1, so the LDS reads of a stage
+  // overlap the MFMAs of its neighbours.  The main loop runs whole rounds of
+  // three steps that all request a stage; the last two to four steps are
+  // straight-line code with the exact request and wait pattern, so no stage is
+  // requested twice and the compiler sees which buffer every request writes.
   constexpr int kPerStep = 2 * NB + 2 * XB;
+#define CLE_STEP_TAIL(NXT)                                                          \
+    CLE_MFMA(1);                                                                    \
+    CLE_READ(NXT, 0);                                                               \
+    half_step_order<NMB, RB>();                                                     \
+    CLE_MFMA(0);                                                                    \
+    CLE_READ(NXT, 1);                                                               \
+    half_step_order<NMB, RB>();
 #define CLE_STEP(CUR, NXT, KT_)                                                     \
   {                                                                                 \
     wait_vmcnt<kPerStep>();                                                         \
     stage_barrier();                                                                \
-    CLE_ISSUE(CUR, min((KT_) + 3, KT - 1));                                         \
-    CLE_MFMA(1);                                                                    \
-    CLE_READ(NXT, 0);                                                               \
-    half_step_order<NMB, NB>();                                                     \
-    CLE_MFMA(0);                                                                    \
-    CLE_READ(NXT, 1);                                                               \
-    half_step_order<NMB, NB>();                                                     \
+    CLE_ISSUE(CUR, (KT_) + 3);                                                      \
+    CLE_STEP_TAIL(NXT)                                                              \
+  }
+#define CLE_STEP_NOREQ(NXT, W)                                                      \
+  {                                                                                 \
+    wait_vmcnt<W>();                                                                \
+    stage_barrier();                                                                \
+    CLE_STEP_TAIL(NXT)                                                              \
   }
 
   static_assert(kStages == 3, "the pipeline below is written for 3 buffers");
   auto& st0 = g_st0<PHASE, WN, NB, PACKED>;
   auto& st1 = g_st1<PHASE, WN, NB, PACKED>;
   auto& st2 = g_st2<PHASE, WN, NB, PACKED>;
+  // (K / 64 < 3 only on small shapes: the prologue then re-requests the last
+  // stage into a buffer no step reads; the final wait covers it.)
   CLE_ISSUE(st0, 0);
   CLE_ISSUE(st1, min(1, KT - 1));
   CLE_ISSUE(st2, min(2, KT - 1));
@@ -486,46 +516,71 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   CLE_MFMA(0);
   CLE_READ(st0, 1);
   int kt = 0;
-  for (; kt + 3 < KT; kt += 3) {
+  for (; kt + 5 < KT; kt += 3) {
     CLE_STEP(st0, st1, kt);
     CLE_STEP(st1, st2, kt + 1);
     CLE_STEP(st2, st0, kt + 2);
   }
-  if (kt + 1 < KT) {
-    CLE_STEP(st0, st1, kt);
-    ++kt;
-  }
-  if (kt + 1 < KT) {
-    CLE_STEP(st1, st2, kt);
+  // stage kt is in st0; steps kt .. KT-2 remain (stages up to min(kt+2, KT-1)
+  // requested)
+  switch (KT - 1 - kt) {
+    case 4:
+      CLE_STEP(st0, st1, kt);
+      CLE_STEP(st1, st2, kt + 1);
+      CLE_STEP_NOREQ(st0, kPerStep);
+      CLE_STEP_NOREQ(st1, 0);
+      break;
+    case 3:
+      CLE_STEP(st0, st1, kt);
+      CLE_STEP_NOREQ(st2, kPerStep);
+      CLE_STEP_NOREQ(st0, 0);
+      break;
+    case 2:
+      CLE_STEP_NOREQ(st1, kPerStep);
+      CLE_STEP_NOREQ(st2, 0);
+      break;
+    case 1:
+      CLE_STEP_NOREQ(st1, 0);
+      break;
+    default:
+      break;
   }
   CLE_MFMA(1);  // slice 1 of the last stage
 #undef CLE_ISSUE
 #undef CLE_READ
 #undef CLE_MFMA
 #undef CLE_STEP
-  wait_vmcnt<0>();  // the clamped requests have landed before buffers are reused
+#undef CLE_STEP_NOREQ
+#undef CLE_STEP_TAIL
+  wait_vmcnt<0>();  // every request has landed before the buffers are reused
 
-  // epilogue: lane holds rows mb*16 + (lane/16)*4 + i, column lane%16 of each block
+  // epilogue: lane holds rows (xb0+mb)*16 + (lane/16)*4 + i, column lane%16 of
+  // each block.  Phase 1 pairs gate block b with up block HB+b of each loading
+  // wavefront; the act columns of consecutive pairs are 16 apart.
   const int g4 = lane / 16;
+  const int col = t.col + cg * RH * 16 * (PHASE == 1 ? HB : NB);
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = mb * 16 + g4 * 4 + i;
+      const int row = (xb0 + mb) * 16 + g4 * 4 + i;
       if (row < t.nrows) {
-        uint16_t* o = t.out + row * t.ldo + t.col;
+        uint16_t* o = t.out + row * t.ldo + col;
         if (PHASE == 1) {
 #pragma unroll
-          for (int b = 0; b < HB; ++b)
-            o[b * 16] = f32_to_bf16(silu(acc[b][mb][i]) * acc[HB + b][mb][i]);
-        } else if (PHASE == 3) {
-          float* of = reinterpret_cast<float*>(t.out) + row * t.ldo + t.col;
+          for (int u = 0; u < RH; ++u)
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-            of[b * 16] = t.bias ? acc[b][mb][i] + t.bias[t.col + b * 16] : acc[b][mb][i];
+            for (int b = 0; b < HB; ++b)
+              o[(u * HB + b) * 16] =
+                  f32_to_bf16(silu(acc[u * NB + b][mb][i]) * acc[u * NB + HB + b][mb][i]);
+        } else if (PHASE == 3) {
+          float* of = reinterpret_cast<float*>(t.out) + row * t.ldo + col;
+#pragma unroll
+          for (int b = 0; b < RB; ++b)
+            of[b * 16] = t.bias ? acc[b][mb][i] + t.bias[col + b * 16] : acc[b][mb][i];
         } else {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) o[b * 16] = f32_to_bf16(acc[b][mb][i]);
+          for (int b = 0; b < RB; ++b) o[b * 16] = f32_to_bf16(acc[b][mb][i]);
         }
       }
     }
@@ -540,6 +595,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
                                                             Weights wts, int H, int I) {
   static_assert(kMB % WN == 0 && WN * NB <= kBlocks && NB % 2 == 0, "tile shape");
   constexpr int HB = NB / 2;
+  constexpr int RH = WN == 8 ? 2 : 1;  // row groups of the compute layout
   const int total = totals[PHASE - 1];
   const int grid = gridDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -580,27 +636,48 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
       wlo = (nt * WN + wave) * (16 * HB);  // gate rows
       whi = I + wlo;                       // up rows of the same act columns
       t.out = static_cast<uint16_t*>(sg.act) + static_cast<int64_t>(row0) * I;
-      t.col = wlo + l16;
+      t.col = nt * WN * 16 * HB + l16;
     } else {
       wlo = (nt * WN + wave) * (16 * NB);
       whi = wlo + 16 * HB;
       t.out = static_cast<uint16_t*>(sg.y) + static_cast<int64_t>(row0) * H;
-      t.col = wlo + l16;
+      t.col = nt * WN * 16 * NB + l16;
     }
     t.ldo = ldo;
     t.bias = nullptr;
     t.wlo = W + static_cast<int64_t>(wlo) * K;
     t.whi = W + static_cast<int64_t>(whi) * K;
-    const int nmb = (t.nrows + 15) / 16;
-    switch (nmb) {
-      case 1: tile_nmb<PHASE, WN, NB, PACKED, 1>(t, wave, lane); break;
-      case 2: tile_nmb<PHASE, WN, NB, PACKED, 2>(t, wave, lane); break;
-      case 3: tile_nmb<PHASE, WN, NB, PACKED, 3>(t, wave, lane); break;
-      case 4: tile_nmb<PHASE, WN, NB, PACKED, 4>(t, wave, lane); break;
-      case 5: tile_nmb<PHASE, WN, NB, PACKED, 5>(t, wave, lane); break;
-      case 6: tile_nmb<PHASE, WN, NB, PACKED, 6>(t, wave, lane); break;
-      case 7: tile_nmb<PHASE, WN, NB, PACKED, 7>(t, wave, lane); break;
-      default: tile_nmb<PHASE, WN, NB, PACKED, 8>(t, wave, lane); break;
+    // row blocks this wavefront computes: its row group's share of the tile
+    const int rg = wave / (WN / RH);
+    const int nmb = min(max((t.nrows + 15) / 16 - rg * (kMB / RH), 0), kMB / RH);
+    if constexpr (RH == 2) {
+      if (rg == 0) {
+        switch (nmb) {
+          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1>(t, wave, lane); break;
+          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2>(t, wave, lane); break;
+          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3>(t, wave, lane); break;
+          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4>(t, wave, lane); break;
+        }
+      } else {
+        switch (nmb) {
+          case 0: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 0>(t, wave, lane); break;
+          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 1>(t, wave, lane); break;
+          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 2>(t, wave, lane); break;
+          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 3>(t, wave, lane); break;
+          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 4>(t, wave, lane); break;
+        }
+      }
+    } else {
+      switch (nmb) {
+        case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1>(t, wave, lane); break;
+        case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2>(t, wave, lane); break;
+        case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3>(t, wave, lane); break;
+        case 4: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4>(t, wave, lane); break;
+        case 5: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 5>(t, wave, lane); break;
+        case 6: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 6>(t, wave, lane); break;
+        case 7: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 7>(t, wave, lane); break;
+        default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 8>(t, wave, lane); break;
+      }
     }
     // every wavefront is done reading the stages before the next tile's
     // first requests overwrite them
@@ -703,14 +780,14 @@ __global__ __launch_bounds__(64 * WN, 1) void gate_gemm_bf16(GateArgs a, int T, 
   const int wlo = (nt * WN + wave) * (16 * NB);
   t.out = reinterpret_cast<uint16_t*>(a.out[j] + static_cast<int64_t>(row0) * E);
   t.ldo = E;
-  t.col = wlo + lane % 16;
+  t.col = nt * WN * 16 * NB + lane % 16;
   t.bias = bias;
   t.wlo = wg + static_cast<int64_t>(wlo) * H;
   t.whi = wg + static_cast<int64_t>(wlo + 16 * HB) * H;
   if (t.nrows > 16)
-    tile_nmb<3, WN, NB, PACKED, 2>(t, wave, lane);
+    tile_nmb<3, WN, NB, PACKED, 1, 0, 2>(t, wave, lane);
   else
-    tile_nmb<3, WN, NB, PACKED, 1>(t, wave, lane);
+    tile_nmb<3, WN, NB, PACKED, 1, 0, 1>(t, wave, lane);
 }
 
 // f32: one thread per logit, sequential K (the small fp32 shapes).
