@@ -315,6 +315,12 @@ constexpr int kBlocks = 16;     // most weight blocks per tile (WN * NB)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gvoid;
+// Global-address-space views for the tile's row-map loads and output stores:
+// through a generic pointer they would be flat instructions, which also count
+// against the LDS counter, so every LDS barrier would wait for them.
+typedef __attribute__((address_space(1))) const int gcint;
+typedef __attribute__((address_space(1))) uint16_t gu16;
+typedef __attribute__((address_space(1))) float gf32;
 
 __device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_slot) {
   __builtin_amdgcn_global_load_lds((gvoid*)(src), (lds_void*)(lds_slot), 16, 0, 0);
@@ -422,7 +428,8 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
     for (int g = 0; g < 2; ++g) {
       // rows past the tile repeat its last row (never stored)
       const int row = min((wave * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
-      const int64_t arow = t.rmap ? static_cast<int64_t>(t.rmap[row] / t.kdiv) : row;
+      const int64_t arow =
+          t.rmap ? static_cast<int64_t>(*(gcint*)(t.rmap + row) / t.kdiv) : row;
       xp[b][g] = t.A + arow * t.K + lc * 8;
     }
   // read side: MFMA operand of lane `lane` for K slice h is row lane%16,
@@ -565,7 +572,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
     for (int i = 0; i < 4; ++i) {
       const int row = (xb0 + mb) * 16 + g4 * 4 + i;
       if (row < t.nrows) {
-        uint16_t* o = t.out + row * t.ldo + col;
+        gu16* o = (gu16*)(t.out + row * t.ldo + col);
         if (PHASE == 1) {
 #pragma unroll
           for (int u = 0; u < RH; ++u)
@@ -574,7 +581,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
               o[(u * HB + b) * 16] =
                   f32_to_bf16(silu(acc[u * NB + b][mb][i]) * acc[u * NB + HB + b][mb][i]);
         } else if (PHASE == 3) {
-          float* of = reinterpret_cast<float*>(t.out) + row * t.ldo + col;
+          gf32* of = (gf32*)(reinterpret_cast<float*>(t.out) + row * t.ldo + col);
 #pragma unroll
           for (int b = 0; b < RB; ++b)
             of[b * 16] = t.bias ? acc[b][mb][i] + t.bias[col + b * 16] : acc[b][mb][i];
