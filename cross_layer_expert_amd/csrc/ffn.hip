@@ -253,6 +253,19 @@ __device__ __forceinline__ int logical_tile_base(int grid) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// The bf16 tiles' SwiGLU epilogue: silu(g) = g / (1 + e^-g) evaluated as
+// g * rcp(1 + 2^(-g log2 e)) with the hardware exp2 and reciprocal (each about
+// 1 ulp of float32, far below the bf16 rounding of Act), and the hardware
+// round-to-nearest-even conversion to bf16.  Six VALU instructions per act
+// value instead of about thirty for expf and an IEEE division, which made the
+// epilogue of a full tile cost several microseconds.
+__device__ __forceinline__ float silu_hw(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+}
+__device__ __forceinline__ uint16_t bf16_hw(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
 // ---------------------------------------------------------------- bf16 MFMA tiles
 // A tile in LDS: [kBM rows][8 chunks of 16 bytes], chunk c of row r stored at
 // c ^ (r & 7) to spread the column reads of 16 rows over the banks.
@@ -564,6 +577,8 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   // epilogue: lane holds rows (xb0+mb)*16 + (lane/16)*4 + i, column lane%16 of
   // each block.  Phase 1 pairs gate block b with up block HB+b of each loading
   // wavefront; the act columns of consecutive pairs are 16 apart.
+  // (the lane's row offset is laundered per tile, like the output stride, so
+  // the compiler does not hoist one register per output row out of the tile loop)
   const int g4 = lane / 16;
   const int col = t.col + cg * RH * 16 * (PHASE == 1 ? HB : NB);
 #pragma unroll
@@ -579,7 +594,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
 #pragma unroll
             for (int b = 0; b < HB; ++b)
               o[(u * HB + b) * 16] =
-                  f32_to_bf16(silu(acc[u * NB + b][mb][i]) * acc[u * NB + HB + b][mb][i]);
+                  bf16_hw(silu_hw(acc[u * NB + b][mb][i]) * acc[u * NB + HB + b][mb][i]);
         } else if (PHASE == 3) {
           gf32* of = (gf32*)(reinterpret_cast<float*>(t.out) + row * t.ldo + col);
 #pragma unroll
@@ -587,7 +602,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
             of[b * 16] = t.bias ? acc[b][mb][i] + t.bias[col + b * 16] : acc[b][mb][i];
         } else {
 #pragma unroll
-          for (int b = 0; b < RB; ++b) o[b * 16] = f32_to_bf16(acc[b][mb][i]);
+          for (int b = 0; b < RB; ++b) o[b * 16] = bf16_hw(acc[b][mb][i]);
         }
       }
     }

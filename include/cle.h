@@ -178,7 +178,8 @@ typedef struct {
  *   w13_shared [L, n_shared, 2I, H], w2_shared [L, n_shared, H, I]: always-on
  *              shared experts (gate weight 1), applied to every x_shared row;
  *              NULL when n_shared == 0.
- *   bf16: fp32 accumulation; Act and Y rounded to bf16 (nearest even).
+ *   bf16: fp32 accumulation; silu from the hardware exp2 and reciprocal
+ *         (about 2 ulp of fp32); Act and Y rounded to bf16 (nearest even).
  *   f32 : fp32 throughout.
  *   w_layout   CLE_W_ROWMAJOR, or CLE_W_PACKED (bf16 only) for all four weight
  *              tensors (see cle_pack_weights).
