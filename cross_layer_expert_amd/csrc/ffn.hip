@@ -25,6 +25,7 @@
 // Consecutive logical tiles go to one XCD (workgroups are dealt round-robin
 // over the 8 XCDs) so tiles reading the same weight rows share that XCD's L2.
 #include <hip/hip_ext.h>
+#include <type_traits>
 
 #include "cle_internal.h"
 
@@ -414,7 +415,10 @@ __device__ __forceinline__ void half_step_order() {
 // RG is this wavefront's row group and NMB the number of 16-row blocks it
 // computes (0 .. 8/RH); both are compile-time values, so the MFMA sequence
 // has no data-dependent branches and every LDS operand offset is a constant.
-template <int PHASE, int WN, int NB, bool PACKED, int RH, int RG, int NMB>
+// TR is the number of K-loop steps left after the last whole round (2 .. 4,
+// fixed by K: 2 + (K/64 - 3) mod 3 for K >= 192), or -1 for code that takes
+// any K; one tail per kernel keeps the register footprint of the loop low.
+template <int PHASE, int WN, int NB, bool PACKED, int RH, int RG, int NMB, int TR>
 __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) {
   static_assert(WN * NB <= kBlocks && WN % RH == 0 && kMB % RH == 0, "weight blocks per tile");
   static_assert(NMB >= 0 && NMB <= kMB / RH && RG >= 0 && RG < RH, "row blocks per wavefront");
@@ -543,7 +547,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   }
   // stage kt is in st0; steps kt .. KT-2 remain (stages up to min(kt+2, KT-1)
   // requested)
-  switch (KT - 1 - kt) {
+  switch (TR >= 0 ? TR : KT - 1 - kt) {
     case 4:
       CLE_STEP(st0, st1, kt);
       CLE_STEP(st1, st2, kt + 1);
@@ -610,7 +614,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   }
 }
 
-template <int PHASE, int WN, int NB, bool PACKED>
+template <int PHASE, int WN, int NB, bool PACKED, int TR>
 __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restrict__ segs,
                                                             int nseg,
                                                             const int* __restrict__ totals,
@@ -675,30 +679,30 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     if constexpr (RH == 2) {
       if (rg == 0) {
         switch (nmb) {
-          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1>(t, wave, lane); break;
-          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2>(t, wave, lane); break;
-          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3>(t, wave, lane); break;
-          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4>(t, wave, lane); break;
+          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1, TR>(t, wave, lane); break;
+          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2, TR>(t, wave, lane); break;
+          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3, TR>(t, wave, lane); break;
+          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4, TR>(t, wave, lane); break;
         }
       } else {
         switch (nmb) {
-          case 0: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 0>(t, wave, lane); break;
-          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 1>(t, wave, lane); break;
-          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 2>(t, wave, lane); break;
-          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 3>(t, wave, lane); break;
-          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 4>(t, wave, lane); break;
+          case 0: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 0, TR>(t, wave, lane); break;
+          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 1, TR>(t, wave, lane); break;
+          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 2, TR>(t, wave, lane); break;
+          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 3, TR>(t, wave, lane); break;
+          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 4, TR>(t, wave, lane); break;
         }
       }
     } else {
       switch (nmb) {
-        case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1>(t, wave, lane); break;
-        case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2>(t, wave, lane); break;
-        case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3>(t, wave, lane); break;
-        case 4: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4>(t, wave, lane); break;
-        case 5: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 5>(t, wave, lane); break;
-        case 6: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 6>(t, wave, lane); break;
-        case 7: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 7>(t, wave, lane); break;
-        default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 8>(t, wave, lane); break;
+        case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1, TR>(t, wave, lane); break;
+        case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2, TR>(t, wave, lane); break;
+        case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3, TR>(t, wave, lane); break;
+        case 4: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4, TR>(t, wave, lane); break;
+        case 5: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 5, TR>(t, wave, lane); break;
+        case 6: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 6, TR>(t, wave, lane); break;
+        case 7: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 7, TR>(t, wave, lane); break;
+        default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 8, TR>(t, wave, lane); break;
       }
     }
     // every wavefront is done reading the stages before the next tile's
@@ -807,9 +811,9 @@ __global__ __launch_bounds__(64 * WN, 1) void gate_gemm_bf16(GateArgs a, int T, 
   t.wlo = wg + static_cast<int64_t>(wlo) * H;
   t.whi = wg + static_cast<int64_t>(wlo + 16 * HB) * H;
   if (t.nrows > 16)
-    tile_nmb<3, WN, NB, PACKED, 1, 0, 2>(t, wave, lane);
+    tile_nmb<3, WN, NB, PACKED, 1, 0, 2, -1>(t, wave, lane);
   else
-    tile_nmb<3, WN, NB, PACKED, 1, 0, 1>(t, wave, lane);
+    tile_nmb<3, WN, NB, PACKED, 1, 0, 1, -1>(t, wave, lane);
 }
 
 // f32: one thread per logit, sequential K (the small fp32 shapes).
@@ -961,24 +965,40 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
     }
     return !e0 || (hipEventRecord(e0, s) == hipSuccess && hipEventRecord(e1, s) == hipSuccess);
   };
-  static int occ_b1[64], occ_b2[64], occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64];
-  static int occ_b1p[64], occ_b2p[64], occ_c1p[64], occ_c2p[64];
+  // The 8-wavefront bf16 kernel of a phase, with the K-loop tail its K needs.
+  auto run_wide = [&](auto phase, auto pk, int K, int64_t ub, hipEvent_t e0, hipEvent_t e1) {
+    constexpr int P = decltype(phase)::value;
+    constexpr bool PK = decltype(pk)::value;
+    static int occ_t2[64], occ_t3[64], occ_t4[64], occ_any[64];
+    const int kt = K / kKS;
+    switch (kt >= 3 ? 2 + (kt - 3) % 3 : -1) {
+      case 2: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 2>, occ_t2, 512, ub, e0, e1);
+      case 3: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 3>, occ_t3, 512, ub, e0, e1);
+      case 4: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 4>, occ_t4, 512, ub, e0, e1);
+      default: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, -1>, occ_any, 512, ub, e0, e1);
+    }
+  };
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using PKT = std::true_type;
+  using PKF = std::false_type;
+  static int occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64], occ_c1p[64], occ_c2p[64];
   bool ok;
   if (wide)
-    ok = packed ? run_phase(ffn_gemm_bf16<1, 8, 2, true>, occ_b1p, 512, ub1, ev[0], ev[1])
-                : run_phase(ffn_gemm_bf16<1, 8, 2, false>, occ_b1, 512, ub1, ev[0], ev[1]);
+    ok = packed ? run_wide(P1(), PKT(), H, ub1, ev[0], ev[1])
+                : run_wide(P1(), PKF(), H, ub1, ev[0], ev[1]);
   else if (dt == CLE_BF16)
-    ok = packed ? run_phase(ffn_gemm_bf16<1, 4, 2, true>, occ_c1p, 256, ub1, ev[0], ev[1])
-                : run_phase(ffn_gemm_bf16<1, 4, 2, false>, occ_c1, 256, ub1, ev[0], ev[1]);
+    ok = packed ? run_phase(ffn_gemm_bf16<1, 4, 2, true, -1>, occ_c1p, 256, ub1, ev[0], ev[1])
+                : run_phase(ffn_gemm_bf16<1, 4, 2, false, -1>, occ_c1, 256, ub1, ev[0], ev[1]);
   else
     ok = run_phase(ffn_gemm_f32<1>, occ_f1, 256, ub1, ev[0], ev[1]);
   if (!ok) return CLE_EHIP;
   if (wide)
-    ok = packed ? run_phase(ffn_gemm_bf16<2, 8, 2, true>, occ_b2p, 512, ub2, ev[2], ev[3])
-                : run_phase(ffn_gemm_bf16<2, 8, 2, false>, occ_b2, 512, ub2, ev[2], ev[3]);
+    ok = packed ? run_wide(P2(), PKT(), I, ub2, ev[2], ev[3])
+                : run_wide(P2(), PKF(), I, ub2, ev[2], ev[3]);
   else if (dt == CLE_BF16)
-    ok = packed ? run_phase(ffn_gemm_bf16<2, 4, 2, true>, occ_c2p, 256, ub2, ev[2], ev[3])
-                : run_phase(ffn_gemm_bf16<2, 4, 2, false>, occ_c2, 256, ub2, ev[2], ev[3]);
+    ok = packed ? run_phase(ffn_gemm_bf16<2, 4, 2, true, -1>, occ_c2p, 256, ub2, ev[2], ev[3])
+                : run_phase(ffn_gemm_bf16<2, 4, 2, false, -1>, occ_c2, 256, ub2, ev[2], ev[3]);
   else
     ok = run_phase(ffn_gemm_f32<2>, occ_f2, 256, ub2, ev[2], ev[3]);
   if (!ok) return CLE_EHIP;
