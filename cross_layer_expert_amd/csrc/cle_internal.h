@@ -35,7 +35,8 @@ cle_status launch_combine_many(int n, const void* const* yp, const int* const* d
                                const float* const* gate, int T, int k, int H,
                                const void* const* y_shared, int n_shared,
                                const void* const* residual, void* const* y, cle_dtype dt,
-                               const cle_loop_state* st, hipStream_t s);
+                               const cle_loop_state* st, hipStream_t s,
+                               const void* const* h0 = nullptr);
 // Row RMS normalisation of cle_rmsnorm_many (todo micro-batches only with a state).
 cle_status launch_rmsnorm(int n, const void* const* x, void* const* y, int T, int H, float eps,
                           cle_dtype dt, const cle_loop_state* st, hipStream_t s);

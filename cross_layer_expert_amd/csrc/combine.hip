@@ -58,7 +58,12 @@ struct CombineArgs {
   const void* residual[CLE_MAX_MICROBATCHES];
   void* y[CLE_MAX_MICROBATCHES];
   const cle_loop_state* st;  // non-NULL: only the members of st->runset
+  // With a state and h0: in a step that restarted the loop, y_j = h0_j for
+  // every micro-batch instead (the run starts over from the initial states).
+  const void* h0[CLE_MAX_MICROBATCHES];
+  bool restart;
 };
+static_assert(sizeof(CombineArgs) <= 4096, "kernel argument size");
 
 // KMAX > 0: k <= KMAX slots, whose destinations and gates are held in
 // registers so that all slot rows of a column chunk are requested before the
@@ -67,7 +72,20 @@ struct CombineArgs {
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs args, int T_, int k, int H,
                                                       int n_shared) {
-  if (args.st && !(args.st->runset >> blockIdx.y & 1)) return;  // uniform over the block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + wave;
+  if (args.st) {  // uniform over the block
+    if (args.restart && args.st->restarted) {
+      if (t >= T_) return;
+      const int64_t nv = static_cast<int64_t>(H) * sizeof(T) / 16;
+      const uint4* src = static_cast<const uint4*>(args.h0[blockIdx.y]) + t * nv;
+      uint4* dst = static_cast<uint4*>(args.y[blockIdx.y]) + t * nv;
+      for (int64_t c = lane; c < nv; c += kWave) dst[c] = src[c];
+      return;
+    }
+    if (!(args.st->runset >> blockIdx.y & 1)) return;
+  }
   const T* __restrict__ yp = static_cast<const T*>(args.yp[blockIdx.y]);
   const int* __restrict__ dest = args.dest[blockIdx.y];
   const float* __restrict__ gate = args.gate[blockIdx.y];
@@ -75,9 +93,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs args, int T_, 
   const T* residual = static_cast<const T*>(args.residual[blockIdx.y]);
   T* y = static_cast<T*>(args.y[blockIdx.y]);
   constexpr int N = Vec<T>::N;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + wave;
   if (t >= T_) return;
   const int* drow = dest + static_cast<int64_t>(t) * k;
   const float* grow = gate + static_cast<int64_t>(t) * k;
@@ -183,7 +198,7 @@ cle_status launch_combine_many(int n, const void* const* yp, const int* const* d
                                const float* const* gate, int T, int k, int H,
                                const void* const* y_shared, int n_shared,
                                const void* const* residual, void* const* y, cle_dtype dt,
-                               const cle_loop_state* st, hipStream_t s) {
+                               const cle_loop_state* st, hipStream_t s, const void* const* h0) {
   CombineArgs a;
   for (int j = 0; j < n; ++j) {
     a.yp[j] = yp[j];
@@ -192,8 +207,10 @@ cle_status launch_combine_many(int n, const void* const* yp, const int* const* d
     a.y_shared[j] = y_shared ? y_shared[j] : nullptr;
     a.residual[j] = residual ? residual[j] : nullptr;
     a.y[j] = y[j];
+    a.h0[j] = h0 ? h0[j] : nullptr;
   }
   a.st = st;
+  a.restart = st && h0;
   if (dt == CLE_BF16)
     launch_combine<uint16_t>(a, n, T, k, H, n_shared, s);
   else

@@ -64,6 +64,11 @@ struct PlanArgs {
   // non-NULL: descriptor j runs only if it is in st->runset, at layer
   // st->run_layer[j] (its own layer field and layer_all are unused)
   const cle_loop_state* st;
+  // the launch that plans the last descriptors also orders the whole table
+  // (see order_segments); earlier launches leave these unused
+  int order, nseg, tm, n1, n2;
+  int* totals;
+  int* mscan;
 };
 
 // Expert weight tensors of a launch; a segment names its matrices by index.
@@ -81,6 +86,49 @@ static_assert(sizeof(PlanArgs) <= 4096, "kernel argument size");
 __device__ __forceinline__ void seg_range(const DescDev& d, int e, int& lo, int& hi) {
   lo = min(max(d.offsets[e], 0), d.rows);
   hi = min(max(d.offsets[e + 1], lo), d.rows);
+}
+
+// One block over the grouped segment table: the row-tile prefix M over the
+// segments (mscan[s] = row tiles of segments before s), then per segment its
+// group's start m0 = M at the group's first segment, the group's row tiles
+// gmt and its own offset moff in the group.  Group g of m-tile start m0
+// owns tiles [N * m0, N * (m0 + gmt)) of a phase with N column tiles, in
+// column-tile-major order.  Runs at the end of the last planning launch,
+// after a block barrier, so the segments this block wrote are visible.
+__device__ __forceinline__ void order_segments(Seg* __restrict__ segs, int nseg, int tm, int n1,
+                                               int n2, int* __restrict__ totals,
+                                               int* __restrict__ mscan, int* part) {
+  const int tid = threadIdx.x;
+  const int per = (nseg + 1023) / 1024;
+  const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
+  int c = 0;
+  for (int s = lo; s < hi; ++s) c += (segs[s].rows + tm - 1) / tm;
+  part[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += a;
+    __syncthreads();
+  }
+  int m = part[tid] - c;
+  for (int s = lo; s < hi; ++s) {
+    mscan[s] = m;
+    m += (segs[s].rows + tm - 1) / tm;
+  }
+  if (tid == 1023) {
+    mscan[nseg] = m;
+    totals[0] = n1 * m;
+    totals[1] = n2 * m;
+  }
+  __syncthreads();
+  for (int s = lo; s < hi; ++s) {
+    const int s0 = s - segs[s].grank, s1 = s0 + segs[s].gsize;
+    const int m0 = mscan[s0];
+    segs[s].m0 = m0;
+    segs[s].gmt = mscan[s1] - m0;
+    segs[s].moff = mscan[s] - m0;
+  }
 }
 
 // Writes the segments of descriptors [c0, c0 + nd) at their grouped
@@ -168,48 +216,10 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
     g.pad = 0;
     segs[pbase[jl] + e * pcnt[jl] + prank[jl]] = g;
   }
-}
-
-// One block over the grouped segment table: the row-tile prefix M over the
-// segments (mscan[s] = row tiles of segments before s), then per segment its
-// group's start m0 = M at the group's first segment, the group's row tiles
-// gmt and its own offset moff in the group.  Group g of m-tile start m0
-// owns tiles [N * m0, N * (m0 + gmt)) of a phase with N column tiles, in
-// column-tile-major order.
-__global__ __launch_bounds__(1024) void ffn_order(Seg* __restrict__ segs, int nseg, int tm,
-                                                  int n1, int n2, int* __restrict__ totals,
-                                                  int* __restrict__ mscan) {
-  __shared__ int part[1024];
-  const int tid = threadIdx.x;
-  const int per = (nseg + 1023) / 1024;
-  const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
-  int c = 0;
-  for (int s = lo; s < hi; ++s) c += (segs[s].rows + tm - 1) / tm;
-  part[tid] = c;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int a = tid >= off ? part[tid - off] : 0;
+  if (p.order) {
+    __shared__ int part[1024];
     __syncthreads();
-    part[tid] += a;
-    __syncthreads();
-  }
-  int m = part[tid] - c;
-  for (int s = lo; s < hi; ++s) {
-    mscan[s] = m;
-    m += (segs[s].rows + tm - 1) / tm;
-  }
-  if (tid == 1023) {
-    mscan[nseg] = m;
-    totals[0] = n1 * m;
-    totals[1] = n2 * m;
-  }
-  __syncthreads();
-  for (int s = lo; s < hi; ++s) {
-    const int s0 = s - segs[s].grank, s1 = s0 + segs[s].gsize;
-    const int m0 = mscan[s0];
-    segs[s].m0 = m0;
-    segs[s].gmt = mscan[s1] - m0;
-    segs[s].moff = mscan[s] - m0;
+    order_segments(segs, p.nseg, p.tm, p.n1, p.n2, p.totals, p.mscan, part);
   }
 }
 
@@ -944,9 +954,15 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
     p.esz = esz;
     p.L = L;
     p.st = st;
+    p.order = c + kPlanDescs >= n_desc;
+    p.nseg = nseg;
+    p.tm = tm;
+    p.n1 = I / tn1;
+    p.n2 = H / tn2;
+    p.totals = totals;
+    p.mscan = mscan;
     ffn_plan<<<dim3(1), dim3(1024), 0, s>>>(p, segs);
   }
-  ffn_order<<<dim3(1), dim3(1024), 0, s>>>(segs, nseg, tm, I / tn1, H / tn2, totals, mscan);
   const Weights wts{w13, w2, w13_shared, w2_shared};
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   if (phase_events)

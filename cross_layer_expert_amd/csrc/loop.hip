@@ -355,23 +355,6 @@ __global__ void loop_init_kernel(LoopInitArgs a) {
   }
 }
 
-struct RestartArgs {
-  const uint4* h0[kMaxN];
-  uint4* h[kMaxN];
-  const cle_loop_state* st;
-  int64_t vecs;  // 16-byte vectors per micro-batch
-};
-
-// h_j = h0_j for every micro-batch, only in a step that restarted the loop.
-__global__ __launch_bounds__(256) void restart_copy_kernel(RestartArgs a) {
-  if (!a.st->restarted) return;
-  const uint4* __restrict__ src = a.h0[blockIdx.y];
-  uint4* __restrict__ dst = a.h[blockIdx.y];
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < a.vecs;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    dst[i] = src[i];
-}
-
 bool valid_policy(int p) { return p >= CLE_POLICY_B0_ALONE && p <= CLE_POLICY_DIFFPEAK; }
 
 }  // namespace
@@ -535,17 +518,7 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
   }
   rc = launch_combine_many(n, const_cast<const void* const*>(reinterpret_cast<void* const*>(d->yp)),
                            d->dest, d->gate, T, k, H, ns > 0 ? ysh : nullptr, ns, res, d->h, dt,
-                           st, s);
+                           st, s, d->restart ? d->h0 : nullptr);
   if (rc != CLE_OK) return rc;
-  if (d->restart) {
-    RestartArgs ra;
-    for (int j = 0; j < n; ++j) {
-      ra.h0[j] = static_cast<const uint4*>(d->h0[j]);
-      ra.h[j] = static_cast<uint4*>(d->h[j]);
-    }
-    ra.st = st;
-    ra.vecs = static_cast<int64_t>(T) * H * (dt == CLE_BF16 ? 2 : 4) / 16;
-    restart_copy_kernel<<<dim3(64, n), dim3(256), 0, s>>>(ra);
-  }
   return launch_status();
 }
