@@ -16,8 +16,11 @@ struct Vec;
 template <>
 struct Vec<uint16_t> {
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t* p, float* f) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+  // 16 bytes as loaded: 8 bf16 values, widened only when used, so the k slot
+  // rows in flight take 4 registers each instead of 8
+  using Raw = uint4;
+  __device__ static Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void unpack(const Raw& v, float* f) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -25,6 +28,7 @@ struct Vec<uint16_t> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ static void load(const uint16_t* p, float* f) { unpack(load_raw(p), f); }
   __device__ static void store(uint16_t* p, const float* f) {
     uint32_t w[4];
 #pragma unroll
@@ -37,13 +41,15 @@ struct Vec<uint16_t> {
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
-  __device__ static void load(const float* p, float* f) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
+  using Raw = float4;
+  __device__ static Raw load_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static void unpack(const Raw& v, float* f) {
     f[0] = v.x;
     f[1] = v.y;
     f[2] = v.z;
     f[3] = v.w;
   }
+  __device__ static void load(const float* p, float* f) { unpack(load_raw(p), f); }
   __device__ static void store(float* p, const float* f) {
     *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
   }
@@ -110,15 +116,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs args, int T_, 
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.0f;
     if (KMAX > 0) {
-      float v[KMAX > 0 ? KMAX : 1][N];
+      typename Vec<T>::Raw raw[KMAX > 0 ? KMAX : 1];
 #pragma unroll
       for (int s = 0; s < KMAX; ++s)
-        if (d[s] >= 0) Vec<T>::load(yp + static_cast<int64_t>(d[s]) * H + c, v[s]);
+        if (d[s] >= 0) raw[s] = Vec<T>::load_raw(yp + static_cast<int64_t>(d[s]) * H + c);
 #pragma unroll
       for (int s = 0; s < KMAX; ++s)
         if (d[s] >= 0) {
+          float v[N];
+          Vec<T>::unpack(raw[s], v);
 #pragma unroll
-          for (int i = 0; i < N; ++i) acc[i] = fmaf(g[s], v[s][i], acc[i]);
+          for (int i = 0; i < N; ++i) acc[i] = fmaf(g[s], v[i], acc[i]);
         }
     } else {
       for (int s = 0; s < k; ++s) {
