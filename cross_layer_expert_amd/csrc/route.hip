@@ -36,15 +36,33 @@ __device__ __forceinline__ float from_ord_bits(uint32_t o) {
   return __uint_as_float(b);
 }
 
+// One DPP step of the wave-wide unsigned 64-bit max: each lane takes the max
+// of its key and the key DPP control CTRL moves to it (rows of ROW_MASK only;
+// a lane whose source is outside its row reads 0, the neutral key).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xf, true));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v >> 32), CTRL, ROW_MASK, 0xf, true));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Max of the 64 lanes' keys, in every lane: shifts by 1, 2, 4 and 8 lanes
+// leave each 16-lane row's max in its last lane, the broadcasts of lanes 15
+// and 31 carry it into the following rows, and lane 63 ends with the max of
+// all (register-to-register moves instead of LDS permutes).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), 63);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 template <int VPL>
@@ -74,7 +92,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E
       key[v] = (static_cast<uint64_t>(ord_bits(row[e])) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
   }
 
-  double z0 = 0.0, total = 0.0;
+  double z0 = 0.0;
   for (int s = 0; s < k; ++s) {
     uint64_t best = key[0];
 #pragma unroll
@@ -89,11 +107,20 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E
     zsel[wave][s] = z;
     esel[wave][s] = e;
     if (s == 0) z0 = static_cast<double>(z);
-    total += exp(static_cast<double>(z) - z0);  // slot order
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // The k terms exp(z_s - z0) in float64, slot s on lane s % 64, summed in
+  // slot order (the same sum, term for term, as a serial loop over s).
+  double total = 0.0;
+  for (int s0 = 0; s0 < k; s0 += kWave) {
+    const int s = s0 + lane;
+    const double ex = s < k ? exp(static_cast<double>(zsel[wave][s]) - z0) : 0.0;
+    const int m = min(kWave, k - s0);
+    for (int q = 0; q < m; ++q) total += __shfl(ex, q, kWave);
+  }
 
   int* irow = idx + static_cast<int64_t>(t) * k;
   float* grow = gate + static_cast<int64_t>(t) * k;
