@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "cle.h"
@@ -100,7 +101,11 @@ struct Seg {
   int16_t gsize;        // segments in the group
   int32_t pad;
 };
-static_assert(sizeof(Seg) == 64, "Seg layout");
+// (kdiv/kkey and grank/gsize are read in pairs as 32-bit words, low half first)
+static_assert(sizeof(Seg) == 64 && offsetof(Seg, kdiv) % 4 == 0 &&
+                  offsetof(Seg, kkey) == offsetof(Seg, kdiv) + 2 &&
+                  offsetof(Seg, grank) % 4 == 0 && offsetof(Seg, gsize) == offsetof(Seg, grank) + 2,
+              "Seg layout");
 
 constexpr size_t kFfnHeader = 256;  // totals live in the first 256 bytes
 

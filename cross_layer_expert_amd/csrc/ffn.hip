@@ -243,7 +243,11 @@ __device__ __forceinline__ TilePos locate_tile(const Seg* segs, int nseg, int ti
   const int m0 = segs[lo].m0, gmt = segs[lo].gmt;
   const int r = tile - N * m0;
   const int nt = r / gmt, q = r % gmt;
-  int s = lo - segs[lo].grank;
+  // grank is read with its neighbour as one 32-bit word: a 16-bit load would
+  // be a vector load, whose wait would also wait for every operand load in flight
+  int32_t gw;
+  __builtin_memcpy(&gw, &segs[lo].grank, sizeof(gw));
+  int s = lo - static_cast<int16_t>(gw & 0xffff);
   while (q >= segs[s].moff + (segs[s].rows + tm - 1) / tm) ++s;
   return TilePos{s, nt, q - segs[s].moff};
 }
@@ -428,8 +432,16 @@ __device__ __forceinline__ void half_step_order() {
 // TR is the number of K-loop steps left after the last whole round (2 .. 4,
 // fixed by K: 2 + (K/64 - 3) mod 3 for K >= 192), or -1 for code that takes
 // any K; one tail per kernel keeps the register footprint of the loop low.
-template <int PHASE, int WN, int NB, bool PACKED, int RH, int RG, int NMB, int TR>
-__device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) {
+// hook() runs once the tile's first three stages are requested, while they
+// are in flight (the persistent loop looks up its next tile there).
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <int PHASE, int WN, int NB, bool PACKED, int RH, int RG, int NMB, int TR,
+          typename Hook = NoHook>
+__device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane,
+                                         const Hook& hook = Hook()) {
   static_assert(WN * NB <= kBlocks && WN % RH == 0 && kMB % RH == 0, "weight blocks per tile");
   static_assert(NMB >= 0 && NMB <= kMB / RH && RG >= 0 && RG < RH, "row blocks per wavefront");
   constexpr int XB = kMB / WN;  // A row blocks loaded by each wavefront
@@ -544,6 +556,7 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane) 
   CLE_ISSUE(st0, 0);
   CLE_ISSUE(st1, min(1, KT - 1));
   CLE_ISSUE(st2, min(2, KT - 1));
+  hook();
   wait_vmcnt<2 * kPerStep>();
   stage_barrier();
   CLE_READ(st0, 0);
@@ -639,17 +652,29 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
   const int l16 = lane % 16;
   const int K = PHASE == 1 ? H : I;
 
-  for (int tile = logical_tile_base(grid); tile < total; tile += grid) {
-    // column tiles of the phase: 16 * NB weight rows per wavefront (phase 1:
-    // half gate, half up rows of 8 * NB act columns)
-    const int ncols = PHASE == 1 ? I / (WN * 8 * NB) : H / (WN * 16 * NB);
-    const TilePos tp = locate_tile(segs, nseg, tile, ncols, kTM);
+  // column tiles of the phase: 16 * NB weight rows per wavefront (phase 1:
+  // half gate, half up rows of 8 * NB act columns)
+  const int ncols = PHASE == 1 ? I / (WN * 8 * NB) : H / (WN * 16 * NB);
+  int tile = logical_tile_base(grid);
+  // the next tile is looked up (scalar loads) while this tile's first stages
+  // are in flight
+  TilePos next = tile < total ? locate_tile(segs, nseg, tile, ncols, kTM) : TilePos{0, 0, 0};
+  for (; tile < total; tile += grid) {
+    const TilePos tp = next;
+    const int tnext = tile + grid;
+    const auto look_ahead = [&]() {
+      if (tnext < total) next = locate_tile(segs, nseg, tnext, ncols, kTM);
+    };
     const Seg sg = segs[tp.si];
     const int nt = tp.nt, mi = tp.mi;
     const int row0 = mi * kTM;
     TileArgs t;
     t.K = K;
-    t.rot = sg.kkey % (K / kKS);
+    // kdiv and kkey read as one 32-bit word (scalar load; see locate_tile)
+    int32_t kw;
+    __builtin_memcpy(&kw, &segs[tp.si].kdiv, sizeof(kw));
+    const int kdiv = static_cast<int16_t>(kw & 0xffff), kkey = (kw >> 16) & 0xffff;
+    t.rot = kkey % (K / kKS);
     t.nrows = min(kTM, sg.rows - row0);
     // The output row stride is laundered per tile: otherwise the compiler
     // hoists every per-row output offset (row * stride, one register per
@@ -659,7 +684,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     if (PHASE == 1 && sg.rmap) {
       t.A = sg.a;
       t.rmap = sg.rmap + row0;
-      t.kdiv = sg.kdiv;
+      t.kdiv = kdiv;
     } else {
       t.A = (PHASE == 1 ? sg.a : static_cast<const uint16_t*>(sg.act)) +
             static_cast<int64_t>(row0) * K;
@@ -689,30 +714,30 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     if constexpr (RH == 2) {
       if (rg == 0) {
         switch (nmb) {
-          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1, TR>(t, wave, lane); break;
-          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2, TR>(t, wave, lane); break;
-          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3, TR>(t, wave, lane); break;
-          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4, TR>(t, wave, lane); break;
+          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1, TR>(t, wave, lane, look_ahead); break;
+          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2, TR>(t, wave, lane, look_ahead); break;
+          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3, TR>(t, wave, lane, look_ahead); break;
+          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4, TR>(t, wave, lane, look_ahead); break;
         }
       } else {
         switch (nmb) {
-          case 0: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 0, TR>(t, wave, lane); break;
-          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 1, TR>(t, wave, lane); break;
-          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 2, TR>(t, wave, lane); break;
-          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 3, TR>(t, wave, lane); break;
-          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 4, TR>(t, wave, lane); break;
+          case 0: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 0, TR>(t, wave, lane, look_ahead); break;
+          case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 1, TR>(t, wave, lane, look_ahead); break;
+          case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 2, TR>(t, wave, lane, look_ahead); break;
+          case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 3, TR>(t, wave, lane, look_ahead); break;
+          default: tile_nmb<PHASE, WN, NB, PACKED, RH, 1, 4, TR>(t, wave, lane, look_ahead); break;
         }
       }
     } else {
       switch (nmb) {
-        case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1, TR>(t, wave, lane); break;
-        case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2, TR>(t, wave, lane); break;
-        case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3, TR>(t, wave, lane); break;
-        case 4: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4, TR>(t, wave, lane); break;
-        case 5: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 5, TR>(t, wave, lane); break;
-        case 6: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 6, TR>(t, wave, lane); break;
-        case 7: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 7, TR>(t, wave, lane); break;
-        default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 8, TR>(t, wave, lane); break;
+        case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1, TR>(t, wave, lane, look_ahead); break;
+        case 2: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 2, TR>(t, wave, lane, look_ahead); break;
+        case 3: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 3, TR>(t, wave, lane, look_ahead); break;
+        case 4: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 4, TR>(t, wave, lane, look_ahead); break;
+        case 5: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 5, TR>(t, wave, lane, look_ahead); break;
+        case 6: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 6, TR>(t, wave, lane, look_ahead); break;
+        case 7: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 7, TR>(t, wave, lane, look_ahead); break;
+        default: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 8, TR>(t, wave, lane, look_ahead); break;
       }
     }
     // every wavefront is done reading the stages before the next tile's

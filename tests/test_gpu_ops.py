@@ -303,6 +303,18 @@ def test_ffn_bf16_cross_layer(H, I):
     _check_ffn(case)
 
 
+@pytest.mark.parametrize("H,I", [(256, 384), (512, 640), (768, 128), (1280, 256)])
+def test_ffn_bf16_k_loop_tails(H, I):
+    """The 8-wavefront tiles at every K-loop tail they can meet: K / 64 =
+    4, 8, 12, 20 (gate/up) and 6, 10, 2, 4 (down), i.e. tails of 4, 3 and 2
+    steps after zero, one or several whole rounds of three, and the short-K
+    path whose prologue re-requests its last stage."""
+    print(f"[ffn tails] bf16 H={H} I={I}", flush=True)
+    case = _ffn_case("bf16", H, I, 8, 2, 0, [1, 0], [SIZES_A, SIZES_B], seed=11)
+    _run_ffn(case)
+    _check_ffn(case)
+
+
 def test_ffn_bf16_shared_experts():
     case = _ffn_case("bf16", 128, 128, 8, 2, 2, [1, 0], [SIZES_A, SIZES_C], seed=4, T_shared=70)
     _run_ffn(case)

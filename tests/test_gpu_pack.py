@@ -93,9 +93,11 @@ def _ffn(H, I, E, L, ns, layers, sizes_list, packed_too=True, seed=3):
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("H,I,ns", [(128, 64, 0), (256, 128, 0), (128, 192, 1), (2048, 768, 0)])
+@pytest.mark.parametrize("H,I,ns", [(128, 64, 0), (256, 128, 0), (128, 192, 1), (2048, 768, 0),
+                                     (512, 640, 0), (1280, 256, 0)])
 def test_ffn_packed_equals_rowmajor(H, I, ns):
-    """Wide and narrow tiles, shared experts, the Qwen3 reduction lengths."""
+    """Wide and narrow tiles, shared experts, the Qwen3 reduction lengths and
+    the other K-loop tails of the wide tiles."""
     print(f"[ffn packed] H={H} I={I} ns={ns}", flush=True)
     E = 8
     sizes = [[0, 1, 63, 64, 65, 130, 7, 0], [200, 0, 0, 0, 0, 0, 0, 3], [16] * 8]
