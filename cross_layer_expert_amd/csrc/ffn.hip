@@ -37,7 +37,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 64;        // rows per tile of the f32 path
 constexpr int kBNF = 64;       // columns per tile of the f32 path (both phases)
-constexpr int kBK = 64;        // K per pipeline step
 constexpr int kPlanDescs = 16;
 constexpr int kXcds = 8;
 

@@ -51,7 +51,7 @@ struct SchedLDS {
 };
 
 __device__ uint64_t pad_to_m(uint64_t chosen, uint64_t ready, int m) {
-  for (int j = 0; j < kMaxN && __popcll(chosen) < m; ++j) {
+  for (int j = 0; j < kMaxN && static_cast<int>(__popcll(chosen)) < m; ++j) {
     const uint64_t b = 1ull << j;
     if ((ready & b) && !(chosen & b)) chosen |= b;
   }
