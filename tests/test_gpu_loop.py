@@ -128,26 +128,40 @@ def test_loop_equals_host_driven(name, policy):
     assert np.array_equal(dl.w_dev.cpu().numpy(), host.w_dev.cpu().numpy())
 
 
-def test_loop_restart_replays_first_run():
-    cfg = _cfg("qwen3-small")
+@pytest.mark.parametrize("name,prenorm,gated", [("qwen3-small", False, False), ("tiny", False, False),
+                                                 ("qwen3-small", True, True)])
+def test_loop_restart_replays_first_run(name, prenorm, gated):
+    """The step that finishes the last micro-batch restarts the loop (the
+    combine writes h <- h0 there): the states are h0 again, and the next run
+    replays the first one step for step (f32 tiles; bf16 with the pre-norm
+    block and routing through the router)."""
+    cfg = _cfg(name)
     W, lt, ht = _inputs(cfg, 8)
-    Wk = tuple(None if w is None else cle.pack_weights(w) for w in W)
-    print("[loop] restart", flush=True)
-    one = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_CUMUTIL, cfg.m, packed=True).run()
+    packed = cfg.dtype == "bf16"
+    Wk = tuple(None if w is None else cle.pack_weights(w) for w in W) if packed else tuple(W)
+    kw = dict(packed=packed, prenorm=prenorm)
+    if gated:
+        dev = device()
+        kw["gate"] = (cle.pack_weights(synth.gate_weights_torch(cfg, 8, dev)),
+                      torch.from_numpy(synth.gate_bias(cfg, 8)).to(dev))
+        lt = None
+    print(f"[loop] restart {name} prenorm={prenorm} gated={gated}", flush=True)
+    one = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_CUMUTIL, cfg.m, **kw).run()
     steps = len(one.trace)
-    rs = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_CUMUTIL, cfg.m, packed=True,
-                device_loop=True, restart=True)
+    rs = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_CUMUTIL, cfg.m, device_loop=True,
+                restart=True, **kw)
     for _ in range(steps):
         rs.step()
     st = rs.sync_trace()
     assert st.restarts == 1 and rs.trace == one.trace
     assert np.array_equal(bits_of(rs.h), bits_of(ht))          # back to h0
-    part = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_CUMUTIL, cfg.m, packed=True)
+    part = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_CUMUTIL, cfg.m, **kw)
     for _ in range(5):
         part.step()
         rs.step()
     rs.sync_trace()
     assert rs.trace[steps:] == part.trace
+    assert np.array_equal(bits_of(rs.h), bits_of(part.h))
     assert np.array_equal(bits_of(rs.h), bits_of(part.h))
     acc = rs.stats()[0]
     assert acc[3] == steps + 5 and acc[:3] == [a + b for a, b in
