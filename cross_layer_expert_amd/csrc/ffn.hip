@@ -603,8 +603,6 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane,
   // epilogue: lane holds rows (xb0+mb)*16 + (lane/16)*4 + i, column lane%16 of
   // each block.  Phase 1 pairs gate block b with up block HB+b of each loading
   // wavefront; the act columns of consecutive pairs are 16 apart.
-  // (the lane's row offset is laundered per tile, like the output stride, so
-  // the compiler does not hoist one register per output row out of the tile loop)
   const int g4 = lane / 16;
   const int col = t.col + cg * RH * 16 * (PHASE == 1 ? HB : NB);
 #pragma unroll
