@@ -316,10 +316,9 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 // the SwiGLU epilogue is local).  Per K slice a wavefront then reads 4 A and
 // 4 weight fragments from LDS instead of 8 + 2, which takes a fifth off the
 // LDS reads that compete with the direct loads for the LDS port (measured
-// together with the exact K-loop tail below:
-// gate/up unchanged on the Qwen3 step, down 4 % and long-prefill phases 5-7 %
-// faster).  Shapes that do not divide into it use WN = 4 x NB = 2, one row
-// group.  (Four wavefronts x four blocks, one wavefront per SIMD, measured
+// together with the exact K-loop tail below: gate/up unchanged on the Qwen3
+// step, down 4 % and long-prefill phases 5-7 % faster).  Shapes that do not
+// divide into it use WN = 4 x NB = 2, one row group.  (Four wavefronts x four blocks, one wavefront per SIMD, measured
 // slower: the memory and barrier stalls of a stage are not hidden.)
 //
 //  * Operands move with direct global->LDS loads (global_load_lds_dwordx4, no
