@@ -21,7 +21,8 @@ Prints one JSON line (rank 0):
   cpu_baseline the CPU oracle on (micro-batch, layer) units of the same
              workload, on this host's cores (and on one core).
 With --sweep it prints instead the 1-u sweep over n, m/n and D and the
-consecutive-layer same-peak counts, one JSON line per (config, D).
+consecutive-layer same-peak counts, one JSON line per (config, D); with
+--group-fit, the per-group expert time against the group workload w_d.
 """
 from __future__ import annotations
 
@@ -273,6 +274,140 @@ def sweep(seed, dev, configs=("qwen3", "moonlight", "taskshift"), ns=(2, 4, 8, 1
             print(json.dumps(line), flush=True)
 
 
+def fit_linear(X, y):
+    """Least squares y ~ X @ c (X includes a column of ones for an intercept):
+    (c, R^2, median |relative residual|)."""
+    X, y = np.asarray(X, np.float64), np.asarray(y, np.float64)
+    c, *_ = np.linalg.lstsq(X, y, rcond=None)
+    r = y - X @ c
+    ss = float(((y - y.mean()) ** 2).sum())
+    r2 = 1.0 - float((r ** 2).sum()) / ss if ss > 0 else 1.0
+    return c, r2, float(np.median(np.abs(r) / np.maximum(np.abs(y), 1e-30)))
+
+
+def group_fit(cfg, seed, dev, reps=3, n_sets=96):
+    """Eq. (2) of EasyBalance on this GPU: the expert time of one group's share
+    of a step, against its workload w_d.
+
+    Under expert parallelism GPU d runs only the segments of group d's experts
+    (E/D of them per layer).  Each point here is one grouped expert launch
+    (both GEMM phases, timed by the launch's own start/end events) over exactly
+    those segments -- the other experts get empty ranges -- for either one
+    (micro-batch, layer) unit or a cross-layer set of m units (distinct
+    micro-batches at random layers, as a RunSet would be).  Fits
+    time = a + b * w_d, and time = a + b * w_d + c * (experts with rows), and
+    checks, per unit or set, whether the group with the largest w_d is also the
+    slowest.  Points run in a seeded random order, so consecutive launches
+    rarely share a layer's weights in the caches."""
+    import torch
+    import cross_layer_expert_amd as cle
+    from cross_layer_expert_amd.engine import Engine
+    W, lt, ht, _, _ = setup(cfg, seed, dev)
+    packed = cfg.dtype == "bf16"
+    Wk = tuple(None if w is None else cle.pack_weights(w) for w in W) if packed else W
+    stream = torch.cuda.current_stream()
+    eng = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_B0_ALONE, 1, stream=stream,
+                 packed=packed)
+    hip = HipEvents()
+    G = cfg.E // cfg.D
+    units = [(j, l) for j in range(cfg.n) for l in range(cfg.L)]
+    off, src = {}, {}
+    for j, l in units:
+        saved = eng.l[j]
+        eng.l[j] = l
+        eng.route_dispatch(j)
+        eng.l[j] = saved
+        off[(j, l)] = eng.offsets[j].clone()
+        src[(j, l)] = eng.src[j].clone()
+    torch.cuda.synchronize()
+    off_h = {u: o.cpu().numpy().astype(np.int64) for u, o in off.items()}
+    # what GPU d would receive of unit u: the rows [lo, hi) of group d's
+    # experts, with offsets rebased to 0 (other experts empty)
+    gof = {}
+    for u, o in off.items():
+        oh = off_h[u]
+        for d in range(cfg.D):
+            lo, hi = int(oh[d * G]), int(oh[(d + 1) * G])
+            gof[(u, d)] = (torch.clamp(o, lo, hi) - lo, lo, hi - lo)
+    rng = np.random.default_rng(seed + 1000)
+    sets = [[(u,) for u in units]]
+    m = min(cfg.m, cfg.n)
+    multi = []
+    for _ in range(n_sets):
+        js = rng.choice(cfg.n, size=m, replace=False)
+        multi.append(tuple((int(j), int(rng.integers(cfg.L))) for j in js))
+    sets.append(multi)
+
+    def work(members, d):
+        w = touched = 0
+        for u in members:
+            oh = off_h[u]
+            seg = np.diff(oh[d * G:(d + 1) * G + 1])
+            w += int(seg.sum())
+            touched += int((seg > 0).sum())
+        return w, touched
+
+    results = {}
+    for name, group_sets in (("single", sets[0]), ("cross_layer_sets", sets[1])):
+        pts = [(s_, d) for s_ in group_sets for d in range(cfg.D)]
+        times = np.zeros((reps, len(pts)))
+        for r in range(reps):
+            order = rng.permutation(len(pts))
+            evs = [hip.create(4) for _ in pts]
+            for i in order:
+                members, d = pts[i]
+                descs = []
+                for u in members:
+                    j, l = u
+                    go, lo, rows = gof[(u, d)]
+                    dd = cle.FfnDesc.from_buffer_copy(eng.descs[j])
+                    dd.layer = l
+                    dd.rows = rows
+                    dd.offsets = go.data_ptr()
+                    dd.src = src[u][lo:].data_ptr()
+                    dd.shared_rows = 0
+                    dd.x_shared = dd.act_shared = dd.y_shared = None
+                    descs.append(dd)
+                cle.grouped_expert_ffn(descs, eng.w13, eng.w2, eng.ws_ffn, events=evs[i],
+                                       stream=stream, packed=packed)
+            torch.cuda.synchronize()
+            times[r] = [hip.ms(e[0], e[3]) * 1e3 for e in evs]
+        t = np.median(times, axis=0)                       # us per point
+        wt = np.array([work(members, d) for members, d in pts], np.float64)
+        ones = np.ones(len(pts))
+        c1, r2_1, rel1 = fit_linear(np.stack([ones, wt[:, 0]], 1), t)
+        c2, r2_2, rel2 = fit_linear(np.stack([ones, wt[:, 0], wt[:, 1]], 1), t)
+        tt = t.reshape(len(group_sets), cfg.D)
+        ww = wt[:, 0].reshape(len(group_sets), cfg.D)
+        slow = tt.argmax(axis=1)
+        peak = ww.argmax(axis=1)
+        close = tt[np.arange(len(tt)), peak] >= 0.98 * tt.max(axis=1)
+        qs = np.quantile(wt[:, 0], np.linspace(0, 1, 9))
+        binned = []
+        for b in range(8):
+            sel = (wt[:, 0] >= qs[b]) & ((wt[:, 0] < qs[b + 1]) | (b == 7))
+            if sel.any():
+                binned.append([int(qs[b]), int(qs[b + 1]), round(float(t[sel].mean()), 2)])
+        results[name] = dict(
+            points=len(pts), members=len(group_sets[0]), reps=reps,
+            mean_time_us=round(float(t.mean()), 2),
+            w_octiles_mean_us=binned,
+            w_range=[int(wt[:, 0].min()), int(wt[:, 0].max())],
+            time_us_range=[round(float(t.min()), 2), round(float(t.max()), 2)],
+            fit_a_b=dict(a_us=round(float(c1[0]), 3), b_us_per_row=round(float(c1[1]), 5),
+                         r2=round(r2_1, 4), median_rel_residual=round(rel1, 4)),
+            fit_a_b_c=dict(a_us=round(float(c2[0]), 3), b_us_per_row=round(float(c2[1]), 5),
+                           c_us_per_expert=round(float(c2[2]), 3), r2=round(r2_2, 4),
+                           median_rel_residual=round(rel2, 4)),
+            peak_group_is_slowest=round(float((slow == peak).mean()), 4),
+            peak_group_within_2pct_of_slowest=round(float(close.mean()), 4),
+        )
+    print(json.dumps({"metric": "per-group expert time vs w_d (Eq. 2)",
+                      "config": {"workload": workload_name(cfg), "group_experts_per_layer": G,
+                                 "seed": seed},
+                      **results}), flush=True)
+
+
 def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None, gate=None, prenorm=True):
     """The CPU oracle on (micro-batch, layer) units of the same workload:
     route, dispatch, float64 SwiGLU experts (numpy matmul) and the combine of
@@ -344,6 +479,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="print the 1-u sweep over n, m/n and D (one JSON line per config and D) "
                          "instead of the timed step")
+    ap.add_argument("--group-fit", action="store_true",
+                    help="print the per-group expert time against w_d (one group's share of "
+                         "each unit, as one GPU of an expert-parallel step) instead of the step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -364,6 +502,9 @@ def main():
         sweep(args.seed, dev)
         return
     cfg = synth.CONFIGS[args.config]
+    if args.group_fit:
+        group_fit(cfg, args.seed, dev)
+        return
     m = args.m if args.m is not None else cfg.m
     policy = cle.POLICIES[args.policy]
     if cfg.start_layers and args.policy == "cumutil" and args.m is None:

@@ -29,3 +29,19 @@ def test_same_peak_matches_oracle():
         for run in (1, 2, 3):
             ref = [oracle.same_peak_windows(list(wj), run) for wj in wt]
             assert bench.same_peak(wt, run) == (sum(h for h, _ in ref), sum(w for _, w in ref))
+
+
+def test_fit_linear_recovers_a_line():
+    # exact points on y = 3 + 0.5 x: the fit returns them with R^2 = 1; one
+    # more regressor that is pure noise gets a coefficient near zero
+    rng = np.random.default_rng(7)
+    x = rng.integers(0, 2000, size=200).astype(float)
+    X = np.stack([np.ones_like(x), x], 1)
+    c, r2, rel = bench.fit_linear(X, 3.0 + 0.5 * x)
+    assert np.allclose(c, [3.0, 0.5]) and abs(r2 - 1.0) < 1e-12 and rel < 1e-12
+    z = rng.normal(size=200)
+    y = 3.0 + 0.5 * x + 0.01 * rng.normal(size=200)
+    c2, r2b, _ = bench.fit_linear(np.stack([np.ones_like(x), x, z], 1), y)
+    assert abs(c2[1] - 0.5) < 1e-4 and abs(c2[2]) < 0.01 and r2b > 0.999
+    # constant response: R^2 is defined as 1 (nothing to explain)
+    assert bench.fit_linear(X, np.full(200, 4.0))[1] == 1.0
