@@ -9,6 +9,8 @@
 //
 //   1. count   one block per 1024-assignment chunk: LDS histogram
 //   2. scan    one block: per-expert prefix over chunks, prefix over experts
+//              (when the chunk histograms are small, each scatter block
+//              computes the prefixes it needs itself: one launch fewer)
 //   3. scatter one block per chunk: in-order ranks from wavefront ballots
 //              (lanes that share an expert id find each other with one ballot
 //              per id bit; rank = popcount of the lower lanes in the group)
@@ -129,17 +131,27 @@ __global__ __launch_bounds__(1024) void dispatch_scan(DispatchArgs args, int64_t
   }
 }
 
+// SCAN: the chunk histograms hold raw counts (no scan launch ran): every block
+// computes the expert totals, their exclusive scan and its own chunk's prefix
+// from them (chunks * E <= kScatterScanMax ints: a few dozen reads per thread
+// at most), and block 0 also writes
+// counts, offsets and the source-less tail.  Otherwise they hold the chunk
+// bases that dispatch_scan wrote.
+template <bool SCAN>
 __global__ __launch_bounds__(256) void dispatch_scatter(DispatchArgs args, int64_t A, int E,
-                                                        int id_bits) {
+                                                        int id_bits, int chunks) {
   if (skip(args, blockIdx.y)) return;
   const int* __restrict__ idx = args.idx[blockIdx.y];
   const int* __restrict__ chunk_base = args.hist + blockIdx.y * args.hist_stride;
   int* __restrict__ dest = args.dest[blockIdx.y];
   int* __restrict__ src = args.src[blockIdx.y];
   __shared__ int wcount[kChunkWaves][CLE_MAX_E];
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  for (int i = threadIdx.x; i < kChunkWaves * E; i += blockDim.x) wcount[i / E][i % E] = 0;
+  __shared__ int base_s[SCAN ? CLE_MAX_E : 1];  // (also the prefix partial sums)
+  __shared__ int part[SCAN ? 256 : 1];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  for (int i = tid; i < kChunkWaves * E; i += blockDim.x) wcount[i / E][i % E] = 0;
   __syncthreads();
   const int64_t wbase = static_cast<int64_t>(blockIdx.x) * kDispatchChunk +
                         static_cast<int64_t>(wave) * kPerWave;
@@ -151,11 +163,82 @@ __global__ __launch_bounds__(256) void dispatch_scatter(DispatchArgs args, int64
       if (e >= 0 && e < E) atomicAdd(&wcount[wave][e], 1);
     }
   }
+  if constexpr (SCAN) {
+    // Thread t owns the experts [t R, t R + R), R = ceil(E / 256): their
+    // totals over all chunks and prefixes over the chunks before this one,
+    // then the exclusive scan of the totals over the 256 runs.  With E <= 256
+    // the chunks are first split over G = 256 / E thread groups (partial sums
+    // in LDS), so each thread reads at most ceil(chunks / G) entries.
+    const int bx = static_cast<int>(blockIdx.x);
+    const int R = (E + 255) / 256;
+    const int e0 = min(E, tid * R), e1 = min(E, e0 + R);
+    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};  // R <= 4 (E <= 1024)
+    if (E <= 256) {
+      const int G = 256 / E, e = tid % E, g = tid / E;
+      int t = 0, p = 0;
+      if (g < G) {
+#pragma unroll 4
+        for (int c = g; c < chunks; c += G) {
+          const int v = chunk_base[static_cast<int64_t>(c) * E + e];
+          t += v;
+          p += c < bx ? v : 0;
+        }
+      }
+      part[tid] = t;
+      base_s[tid] = p;
+      __syncthreads();
+      if (tid < E)
+        for (int q = 0; q < G; ++q) {
+          tot[0] += part[q * E + tid];
+          pre[0] += base_s[q * E + tid];
+        }
+      __syncthreads();  // part and base_s are reused below
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + q;
+        if (e < e1)
+          for (int c = 0; c < chunks; ++c) {
+            const int v = chunk_base[static_cast<int64_t>(c) * E + e];
+            tot[q] += v;
+            pre[q] += c < bx ? v : 0;
+          }
+      }
+    }
+    const int run_sum = tot[0] + tot[1] + tot[2] + tot[3];
+    part[tid] = run_sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int add = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    int excl = part[tid] - run_sum;
+    const int nvalid = part[255];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + q;
+      if (e < e1) {
+        base_s[e] = excl + pre[q];
+        if (blockIdx.x == 0) {
+          args.counts[blockIdx.y][e] = tot[q];
+          args.offsets[blockIdx.y][e] = excl;
+        }
+        excl += tot[q];
+      }
+    }
+    if (blockIdx.x == 0) {
+      if (tid == 0) args.offsets[blockIdx.y][E] = nvalid;
+      // positions past the valid assignments (dropped ids) have no source
+      for (int64_t p = nvalid + tid; p < A; p += blockDim.x) src[p] = -1;
+    }
+  }
   __syncthreads();
   // per expert: absolute base of each wave's sub-range
   const int* cb = chunk_base + static_cast<int64_t>(blockIdx.x) * E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = cb[e];
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = SCAN ? base_s[e] : cb[e];
     for (int w = 0; w < kChunkWaves; ++w) {
       const int v = wcount[w][e];
       wcount[w][e] = run;
@@ -229,15 +312,23 @@ namespace cle {
 namespace {
 
 // count, scan and scatter for n micro-batches of A assignments each
+// chunk histogram entries up to which every scatter block does the scan itself
+constexpr int64_t kScatterScanMax = 4096;
+
 cle_status launch_dispatch(const DispatchArgs& a, int n, int64_t A, int E, hipStream_t s) {
   const int64_t chunks = dispatch_chunks(A);
   if (chunks > 0)
     dispatch_count<<<dim3(static_cast<unsigned>(chunks), n), dim3(256), 0, s>>>(a, A, E);
-  dispatch_scan<<<dim3(n), dim3(1024), 0, s>>>(a, chunks, E, A);
+  const bool scan_in_scatter = A > 0 && chunks * E <= kScatterScanMax;
+  if (!scan_in_scatter) dispatch_scan<<<dim3(n), dim3(1024), 0, s>>>(a, chunks, E, A);
   if (A == 0) return launch_status();
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
-  dispatch_scatter<<<dim3(static_cast<unsigned>(chunks), n), dim3(256), 0, s>>>(a, A, E, id_bits);
+  const dim3 grid(static_cast<unsigned>(chunks), n);
+  if (scan_in_scatter)
+    dispatch_scatter<true><<<grid, dim3(256), 0, s>>>(a, A, E, id_bits, static_cast<int>(chunks));
+  else
+    dispatch_scatter<false><<<grid, dim3(256), 0, s>>>(a, A, E, id_bits, static_cast<int>(chunks));
   return launch_status();
 }
 

@@ -53,7 +53,7 @@ def test_route_many(n, T, E, k):
 
 @pytest.mark.parametrize("n,T,k,E,skew", [(3, 2048, 8, 128, 1.1), (64, 7, 3, 16, 2.0),
                                           (2, 1000, 6, 1024, 0.5), (1, 1, 1, 1, 0.0),
-                                          (8, 4097, 2, 7, 3.0)])
+                                          (8, 4097, 2, 7, 3.0), (2, 5000, 8, 128, 1.1)])
 def test_dispatch_many(n, T, k, E, skew):
     dev = device()
     rng = np.random.default_rng(T + n)

@@ -97,7 +97,14 @@ def _dispatch_case(idx, E, H, dtype, seed=0):
 @pytest.mark.parametrize("T,k,E,H,dtype,skew", [
     (16, 2, 8, 64, "f32", 0.0), (2048, 8, 128, 2048, "bf16", 1.1), (1024, 6, 64, 256, "bf16", 1.0),
     (1000, 3, 7, 64, "bf16", 0.0), (333, 8, 1024, 64, "f32", 0.5), (77, 1, 1, 64, "bf16", 0.0),
-    (129, 8, 128, 128, "bf16", 3.0), (1, 1, 4, 64, "f32", 0.0), (4097, 4, 16, 64, "bf16", 2.0)])
+    (129, 8, 128, 128, "bf16", 3.0), (1, 1, 4, 64, "f32", 0.0), (4097, 4, 16, 64, "bf16", 2.0),
+    # up to 4096 chunk-histogram entries (chunks x E) each scatter block does
+    # the scan itself; past that a scan launch does it: both sides of the
+    # limit for E = 128 and E = 1024, E = 300 (two experts per thread), the
+    # long-prefill size and many chunks of few experts
+    (4096, 8, 128, 64, "bf16", 1.1), (4500, 8, 128, 64, "bf16", 1.1),
+    (512, 8, 1024, 64, "bf16", 0.3), (513, 8, 1024, 64, "bf16", 0.3), (700, 5, 300, 64, "f32", 1.0),
+    (16384, 8, 128, 64, "bf16", 1.1), (32769, 1, 5, 64, "f32", 0.0), (3000, 11, 1024, 64, "bf16", 0.3)])
 def test_dispatch_matches_oracle(T, k, E, H, dtype, skew):
     rng = np.random.default_rng(T + E)
     # skewed expert ids: Zipf-like weights over a random permutation
@@ -124,13 +131,15 @@ def test_dispatch_route_chain_qwen3_shape():
     assert np.array_equal(xp, x[rs // cfg.k])
 
 
-def test_dispatch_out_of_range_ids_are_dropped():
-    E, T, k, H = 8, 50, 3, 64
+# the scan in the scatter blocks, then a scan launch (9 chunks x 600 experts)
+@pytest.mark.parametrize("T,E", [(50, 8), (3000, 600)])
+def test_dispatch_out_of_range_ids_are_dropped(T, E):
+    k, H = 3, 64
     rng = np.random.default_rng(5)
     idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
-    bad = [(0, 1), (7, 0), (49, 2), (20, 1)]
+    bad = [(0, 1), (7, 0), (T - 1, 2), (20, 1)]
     for t, s in bad:
-        idx[t, s] = [-1, 8, 1 << 30, -100][bad.index((t, s))]
+        idx[t, s] = [-1, E, 1 << 30, -100][bad.index((t, s))]
     x, counts, offsets, dest, src, xp = _dispatch_case(idx, E, H, "f32")
     valid = (idx >= 0) & (idx < E)
     flat = idx.reshape(-1)
