@@ -25,9 +25,13 @@ int device_cu_count();
 // their arguments already.  `st` (may be NULL) restricts a launch to the
 // micro-batches of the loop state's todo (route, dispatch) or runset
 // (combine, expert FFN) mask; the kernels read the mask on the device.
+// With norm_x, the same launch also writes norm_y[j] = rmsnorm(norm_x[j]) (rows
+// of H elements of norm_dt; the rows of cle_rmsnorm_many, bit for bit).
 cle_status launch_route(int n, const float* const* logits, int T, int E, int k, int* const* idx,
                         float* const* gate, const cle_loop_state* st, int64_t layer_stride,
-                        hipStream_t s);
+                        hipStream_t s, const void* const* norm_x = nullptr,
+                        void* const* norm_y = nullptr, int H = 0, float eps = 0.0f,
+                        cle_dtype norm_dt = CLE_BF16);
 cle_status launch_dispatch_many(int n, const int* const* idx, int T, int k, int E,
                                 int* const* counts, int* const* offsets, int* const* dest,
                                 int* const* src, void* ws, const cle_loop_state* st,

@@ -464,9 +464,11 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
 
   hipStream_t s = as_stream(stream);
   const cle_loop_state* st = d->state;
-  if (d->prenorm) {
-    const void* hs[CLE_MAX_MICROBATCHES];
-    for (int j = 0; j < n; ++j) hs[j] = d->h[j];
+  const void* hs[CLE_MAX_MICROBATCHES];
+  for (int j = 0; j < n; ++j) hs[j] = d->h[j];
+  // with given scores the normalisation rides in the routing launch; the
+  // router GEMM reads the normalised rows, so there it runs first
+  if (d->prenorm && gated) {
     rc = launch_rmsnorm(n, hs, d->xn, T, H, d->norm_eps, dt, st, s);
     if (rc != CLE_OK) return rc;
   }
@@ -485,7 +487,9 @@ extern "C" cle_status cle_loop_step(const cle_loop_desc* d, void* const* phase_e
     rc = launch_route(n, const_cast<const float* const*>(d->gate_logits), T, E, k, d->idx,
                       d->gate, st, 0, s);
   } else {
-    rc = launch_route(n, d->logits, T, E, k, d->idx, d->gate, st, static_cast<int64_t>(T) * E, s);
+    rc = launch_route(n, d->logits, T, E, k, d->idx, d->gate, st, static_cast<int64_t>(T) * E, s,
+                      d->prenorm ? hs : nullptr, d->prenorm ? d->xn : nullptr, H, d->norm_eps,
+                      dt);
   }
   if (rc != CLE_OK) return rc;
   rc = launch_dispatch_many(n, d->idx, T, k, E, d->counts, d->offsets, d->dest, d->src,

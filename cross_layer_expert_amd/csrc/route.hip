@@ -7,7 +7,13 @@
 // so that an unsigned max picks the largest logit and, among equal logits,
 // the smallest expert id.  Each of the k rounds is one wave-wide max; the
 // winner's key is cleared.  Key 0 never belongs to a finite logit.
-#include "cle_internal.h"
+//
+// A launch can also carry the RMS normalisation of the micro-batches' rows
+// (norm_row.h) in blocks of its own after the routing blocks: the two jobs
+// are independent when the scores are given, and one launch does both.
+#include <type_traits>
+
+#include "norm_row.h"
 
 namespace cle {
 namespace {
@@ -23,7 +29,14 @@ struct RouteArgs {
   float* gate[CLE_MAX_MICROBATCHES];
   const cle_loop_state* st;
   int64_t layer_stride;
+  // normalisation blocks (blockIdx.x >= route_blocks): rows of nx[j] into ny[j]
+  const void* nx[CLE_MAX_MICROBATCHES];
+  void* ny[CLE_MAX_MICROBATCHES];
+  int route_blocks;
+  int H;
+  float eps;
 };
+static_assert(sizeof(RouteArgs) <= 4096, "kernel argument size");
 
 __device__ __forceinline__ uint32_t ord_bits(float z) {
   if (z == 0.0f) z = 0.0f;  // -0.0 and +0.0 are the same logit
@@ -65,9 +78,22 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-template <int VPL>
+// NT: element type of the rows to normalise in the same launch, or void.
+template <int VPL, typename NT>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E, int k) {
   const int j = blockIdx.y;
+  if constexpr (!std::is_void<NT>::value) {
+    if (static_cast<int>(blockIdx.x) >= args.route_blocks) {  // uniform over the block
+      if (args.st && !(args.st->todo >> j & 1)) return;
+      const int nwave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+      const int t = (blockIdx.x - args.route_blocks) * kRouteWaves + nwave;
+      if (t >= T) return;
+      const int64_t off = static_cast<int64_t>(t) * args.H;
+      rmsnorm_row<NT>(static_cast<const NT*>(args.nx[j]) + off, static_cast<NT*>(args.ny[j]) + off,
+                      args.H, args.eps, threadIdx.x % kWave);
+      return;
+    }
+  }
   const float* __restrict__ logits = args.logits[j];
   if (args.st) {  // uniform over the block
     if (!(args.st->todo >> j & 1)) return;
@@ -137,36 +163,49 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E
 namespace cle {
 namespace {
 
-cle_status launch_route_args(const RouteArgs& a, int n, int T, int E, int k, hipStream_t s) {
-  const dim3 grid((T + kRouteWaves - 1) / kRouteWaves, n), block(256);
+template <typename NT>
+void launch_route_kernel(const RouteArgs& a, int n, int T, int E, int k, hipStream_t s) {
+  const int rb = (T + kRouteWaves - 1) / kRouteWaves;
+  const dim3 grid(std::is_void<NT>::value ? rb : 2 * rb, n), block(256);
   const int vpl = (E + kWave - 1) / kWave;
   if (vpl <= 1)
-    route_kernel<1><<<grid, block, 0, s>>>(a, T, E, k);
+    route_kernel<1, NT><<<grid, block, 0, s>>>(a, T, E, k);
   else if (vpl <= 2)
-    route_kernel<2><<<grid, block, 0, s>>>(a, T, E, k);
+    route_kernel<2, NT><<<grid, block, 0, s>>>(a, T, E, k);
   else if (vpl <= 4)
-    route_kernel<4><<<grid, block, 0, s>>>(a, T, E, k);
+    route_kernel<4, NT><<<grid, block, 0, s>>>(a, T, E, k);
   else if (vpl <= 8)
-    route_kernel<8><<<grid, block, 0, s>>>(a, T, E, k);
+    route_kernel<8, NT><<<grid, block, 0, s>>>(a, T, E, k);
   else
-    route_kernel<16><<<grid, block, 0, s>>>(a, T, E, k);
-  return launch_status();
+    route_kernel<16, NT><<<grid, block, 0, s>>>(a, T, E, k);
 }
 
 }  // namespace
 
 cle_status launch_route(int n, const float* const* logits, int T, int E, int k, int* const* idx,
                         float* const* gate, const cle_loop_state* st, int64_t layer_stride,
-                        hipStream_t s) {
+                        hipStream_t s, const void* const* norm_x, void* const* norm_y, int H,
+                        float eps, cle_dtype norm_dt) {
   RouteArgs a;
   for (int j = 0; j < n; ++j) {
     a.logits[j] = logits[j];
     a.idx[j] = idx[j];
     a.gate[j] = gate[j];
+    a.nx[j] = norm_x ? norm_x[j] : nullptr;
+    a.ny[j] = norm_y ? norm_y[j] : nullptr;
   }
   a.st = st;
   a.layer_stride = layer_stride;
-  return launch_route_args(a, n, T, E, k, s);
+  a.route_blocks = (T + kRouteWaves - 1) / kRouteWaves;
+  a.H = H;
+  a.eps = eps;
+  if (!norm_x)
+    launch_route_kernel<void>(a, n, T, E, k, s);
+  else if (norm_dt == CLE_BF16)
+    launch_route_kernel<uint16_t>(a, n, T, E, k, s);
+  else
+    launch_route_kernel<float>(a, n, T, E, k, s);
+  return launch_status();
 }
 
 }  // namespace cle
