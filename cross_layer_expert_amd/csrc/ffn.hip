@@ -130,6 +130,48 @@ __device__ __forceinline__ void order_segments(Seg* __restrict__ segs, int nseg,
   }
 }
 
+// order_segments for a table planned by this one block (at most kPlanLds
+// segments), from the rows and group fields the block kept in LDS: no
+// global round trips between the passes.
+constexpr int kPlanLds = 2048;
+__device__ __forceinline__ void order_segments_lds(Seg* __restrict__ segs, int nseg, int tm,
+                                                   int n1, int n2, int* __restrict__ totals,
+                                                   const int* rows_l, const int* grp_l,
+                                                   int* mscan_l, int* part) {
+  const int tid = threadIdx.x;
+  const int per = (nseg + 1023) / 1024;
+  const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
+  int c = 0;
+  for (int s = lo; s < hi; ++s) c += (rows_l[s] + tm - 1) / tm;
+  part[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += a;
+    __syncthreads();
+  }
+  int m = part[tid] - c;
+  for (int s = lo; s < hi; ++s) {
+    mscan_l[s] = m;
+    m += (rows_l[s] + tm - 1) / tm;
+  }
+  if (tid == 1023) {
+    mscan_l[nseg] = m;
+    totals[0] = n1 * m;
+    totals[1] = n2 * m;
+  }
+  __syncthreads();
+  for (int s = lo; s < hi; ++s) {
+    const int grank = static_cast<int16_t>(grp_l[s] & 0xffff), gsize = grp_l[s] >> 16;
+    const int s0 = s - grank, s1 = s0 + gsize;
+    const int m0 = mscan_l[s0];
+    segs[s].m0 = m0;
+    segs[s].gmt = mscan_l[s1] - m0;
+    segs[s].moff = mscan_l[s] - m0;
+  }
+}
+
 // Writes the segments of descriptors [c0, c0 + nd) at their grouped
 // positions.  Descriptors are grouped by layer (ascending; micro-batches not
 // in the loop state's RunSet form a last, empty group); within the group of
@@ -176,6 +218,10 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
     prank[tid] = rank;
   }
   __syncthreads();
+  // one launch plans the whole table: its rows and group fields stay in LDS
+  // for the ordering pass
+  __shared__ int rows_l[kPlanLds], grp_l[kPlanLds], mscan_l[kPlanLds + 1];
+  const bool in_lds = p.order && p.c0 == 0 && p.nseg <= kPlanLds;
   const int64_t H = p.H, I = p.I, esz = p.esz;
   for (int s = tid; s < p.nd * (p.E + p.ns); s += 1024) {
     const int jl = s / (p.E + p.ns), e = s % (p.E + p.ns);
@@ -213,12 +259,20 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
     g.grank = static_cast<int16_t>(prank[jl]);
     g.gsize = static_cast<int16_t>(pcnt[jl]);
     g.pad = 0;
-    segs[pbase[jl] + e * pcnt[jl] + prank[jl]] = g;
+    const int pos = pbase[jl] + e * pcnt[jl] + prank[jl];
+    segs[pos] = g;
+    if (in_lds) {
+      rows_l[pos] = g.rows;
+      grp_l[pos] = (static_cast<int>(g.gsize) << 16) | static_cast<uint16_t>(g.grank);
+    }
   }
   if (p.order) {
     __shared__ int part[1024];
     __syncthreads();
-    order_segments(segs, p.nseg, p.tm, p.n1, p.n2, p.totals, p.mscan, part);
+    if (in_lds)
+      order_segments_lds(segs, p.nseg, p.tm, p.n1, p.n2, p.totals, rows_l, grp_l, mscan_l, part);
+    else
+      order_segments(segs, p.nseg, p.tm, p.n1, p.n2, p.totals, p.mscan, part);
   }
 }
 

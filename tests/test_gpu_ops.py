@@ -324,6 +324,24 @@ def test_ffn_bf16_k_loop_tails(H, I):
     _check_ffn(case)
 
 
+@pytest.mark.parametrize("n_desc,E", [(20, 8), (3, 1024)])
+def test_ffn_plan_beyond_one_planner_table(n_desc, E):
+    """Plans the one planner workgroup cannot keep in LDS: 20 descriptors (two
+    planner launches) and 3 x 1024 segments (more than it holds)."""
+    rng = np.random.default_rng(n_desc + E)
+    sizes_list = []
+    for j in range(n_desc):
+        sizes = np.zeros(E, np.int64)
+        hot = rng.choice(E, min(E, 6), replace=False)
+        sizes[hot] = rng.integers(0, 150, size=hot.size)
+        sizes_list.append(list(sizes))
+    layers = [int(v) for v in rng.integers(0, 3, size=n_desc)]
+    print(f"[ffn plan] n_desc={n_desc} E={E}", flush=True)
+    case = _ffn_case("bf16", 128, 64, E, 3, 0, layers, sizes_list, seed=2)
+    _run_ffn(case)
+    _check_ffn(case)
+
+
 def test_ffn_bf16_shared_experts():
     case = _ffn_case("bf16", 128, 128, 8, 2, 2, [1, 0], [SIZES_A, SIZES_C], seed=4, T_shared=70)
     _run_ffn(case)
