@@ -39,6 +39,10 @@ constexpr int kBM = 64;        // rows per tile of the f32 path
 constexpr int kBNF = 64;       // columns per tile of the f32 path (both phases)
 constexpr int kPlanDescs = 16;
 constexpr int kXcds = 8;
+// the per-XCD tile claim counters of the two phases sit in the workspace
+// header after the tile totals: ints [kClaimsOffset, kClaimsOffset + 16)
+constexpr int kClaimsOffset = 16;
+static_assert((kClaimsOffset + 2 * kXcds) * sizeof(int) <= kFfnHeader, "workspace header");
 
 struct DescDev {
   int layer, rows;
@@ -268,6 +272,7 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
   }
   if (p.order) {
     __shared__ int part[1024];
+    if (tid < 2 * kXcds) p.totals[kClaimsOffset + tid] = 0;  // the GEMMs' tile claims
     __syncthreads();
     if (in_lds)
       order_segments_lds(segs, p.nseg, p.tm, p.n1, p.n2, p.totals, rows_l, grp_l, mscan_l, part);
@@ -401,6 +406,7 @@ typedef __attribute__((address_space(1))) const void gvoid;
 typedef __attribute__((address_space(1))) const int gcint;
 typedef __attribute__((address_space(1))) uint16_t gu16;
 typedef __attribute__((address_space(1))) float gf32;
+typedef __attribute__((address_space(1))) int gint;
 
 __device__ __forceinline__ void dma16(const uint16_t* src, uint4* lds_slot) {
   __builtin_amdgcn_global_load_lds((gvoid*)(src), (lds_void*)(lds_slot), 16, 0, 0);
@@ -687,10 +693,17 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane,
   }
 }
 
+// Tiles go to XCDs in contiguous ranges of ceil(total / 8); within its XCD's
+// range a workgroup takes the tile at (range start + its index among the XCD's
+// workgroups) first, and then whichever tile the XCD's claim counter hands it,
+// so the workgroups of an XCD finish within about one tile of each other
+// whatever the tiles' lengths.  claims: this phase's 8 counters, zeroed by the
+// planner.
 template <int PHASE, int WN, int NB, bool PACKED, int TR>
 __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restrict__ segs,
                                                             int nseg,
                                                             const int* __restrict__ totals,
+                                                            int* __restrict__ claims,
                                                             Weights wts, int H, int I) {
   static_assert(kMB % WN == 0 && WN * NB <= kBlocks && NB % 2 == 0, "tile shape");
   constexpr int HB = NB / 2;
@@ -705,15 +718,39 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
   // column tiles of the phase: 16 * NB weight rows per wavefront (phase 1:
   // half gate, half up rows of 8 * NB act columns)
   const int ncols = PHASE == 1 ? I / (WN * 8 * NB) : H / (WN * 16 * NB);
-  int tile = logical_tile_base(grid);
-  // the next tile is looked up (scalar loads) while this tile's first stages
-  // are in flight
-  TilePos next = tile < total ? locate_tile(segs, nseg, tile, ncols, kTM) : TilePos{0, 0, 0};
-  for (; tile < total; tile += grid) {
+  // grid is a multiple of kXcds; workgroup b runs on XCD b % kXcds
+  const int xcd = blockIdx.x % kXcds, chunk = grid / kXcds;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int lo = min(total, xcd * per), hi = min(total, lo + per);
+  __shared__ int s_next[2][4];  // by tile parity: next tile and its position
+  int tile = lo + static_cast<int>(blockIdx.x) / kXcds;
+  TilePos next = tile < hi ? locate_tile(segs, nseg, tile, ncols, kTM) : TilePos{0, 0, 0};
+  for (int par = 0; tile < hi; par ^= 1) {
     const TilePos tp = next;
-    const int tnext = tile + grid;
+    // Wavefront 0 claims the workgroup's next tile before this tile's first
+    // requests (so the claim has returned once they are in flight), then in
+    // the prologue locates it (scalar loads) and leaves both in LDS, where
+    // the other wavefronts read them after this tile's barriers.
+    int claim = 0;
+    if (wave == 0 && lane == 0) {
+      // a per-lane (vector) address: the counter is not folded into a
+      // wave-aggregated atomic, whose result would be waited for at once
+      gint* cp = (gint*)(claims + xcd);
+      asm volatile("" : "+v"(cp));
+      claim = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int tnext = hi;
     const auto look_ahead = [&]() {
-      if (tnext < total) next = locate_tile(segs, nseg, tnext, ncols, kTM);
+      if (wave == 0) {
+        tnext = lo + chunk + __builtin_amdgcn_readfirstlane(claim);
+        if (tnext < hi) next = locate_tile(segs, nseg, tnext, ncols, kTM);
+        if (lane == 0) {
+          s_next[par][0] = tnext;
+          s_next[par][1] = next.si;
+          s_next[par][2] = next.nt;
+          s_next[par][3] = next.mi;
+        }
+      }
     };
     const Seg sg = segs[tp.si];
     const int nt = tp.nt, mi = tp.mi;
@@ -793,14 +830,20 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     // every wavefront is done reading the stages before the next tile's
     // first requests overwrite them
     stage_barrier();
+    if (wave != 0) {
+      tnext = s_next[par][0];
+      next = TilePos{s_next[par][1], s_next[par][2], s_next[par][3]};
+    }
+    tile = tnext;
   }
 }
 
 // ---------------------------------------------------------------- f32 tiles (exact-order reference path)
 template <int PHASE>
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const Seg* __restrict__ segs, int nseg,
-                                                    const int* __restrict__ totals, Weights wts,
-                                                    int H, int I) {
+                                                    const int* __restrict__ totals,
+                                                    int* __restrict__ /*claims: unused*/,
+                                                    Weights wts, int H, int I) {
   const int total = totals[PHASE - 1];
   const int grid = gridDim.x;
   const int K = PHASE == 1 ? H : I;
@@ -1007,6 +1050,8 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
 
   hipStream_t s = as_stream(stream);
   int* totals = static_cast<int*>(ws);
+  int* claims1 = totals + kClaimsOffset;  // per-XCD tile claims of each phase
+  int* claims2 = claims1 + kXcds;
   Seg* segs = reinterpret_cast<Seg*>(static_cast<char*>(ws) + kFfnHeader);
   const int nseg = n_desc * (E + n_shared);
   int* mscan = reinterpret_cast<int*>(segs + nseg);
@@ -1046,27 +1091,28 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
   // any) are taken by the launch itself, so timing adds no marker between
   // kernels.  A phase without tiles records its event pair back to back.
   auto run_phase = [&](auto kernel, int* occ, int threads, int64_t ub, hipEvent_t e0,
-                       hipEvent_t e1) -> bool {
+                       hipEvent_t e1, int* claims) -> bool {
     if (ub > 0) {
       const int g = persistent_grid(ub, resident_blocks(kernel, occ, threads));
       hipExtLaunchKernelGGL(kernel, dim3(g), dim3(threads), 0, s, e0, e1, 0,
                             static_cast<const Seg*>(segs), nseg,
-                            static_cast<const int*>(totals), wts, H, I);
+                            static_cast<const int*>(totals), claims, wts, H, I);
       return true;
     }
     return !e0 || (hipEventRecord(e0, s) == hipSuccess && hipEventRecord(e1, s) == hipSuccess);
   };
   // The 8-wavefront bf16 kernel of a phase, with the K-loop tail its K needs.
-  auto run_wide = [&](auto phase, auto pk, int K, int64_t ub, hipEvent_t e0, hipEvent_t e1) {
+  auto run_wide = [&](auto phase, auto pk, int K, int64_t ub, hipEvent_t e0, hipEvent_t e1,
+                      int* claims) {
     constexpr int P = decltype(phase)::value;
     constexpr bool PK = decltype(pk)::value;
     static int occ_t2[64], occ_t3[64], occ_t4[64], occ_any[64];
     const int kt = K / kKS;
     switch (kt >= 3 ? 2 + (kt - 3) % 3 : -1) {
-      case 2: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 2>, occ_t2, 512, ub, e0, e1);
-      case 3: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 3>, occ_t3, 512, ub, e0, e1);
-      case 4: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 4>, occ_t4, 512, ub, e0, e1);
-      default: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, -1>, occ_any, 512, ub, e0, e1);
+      case 2: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 2>, occ_t2, 512, ub, e0, e1, claims);
+      case 3: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 3>, occ_t3, 512, ub, e0, e1, claims);
+      case 4: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 4>, occ_t4, 512, ub, e0, e1, claims);
+      default: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, -1>, occ_any, 512, ub, e0, e1, claims);
     }
   };
   using P1 = std::integral_constant<int, 1>;
@@ -1076,22 +1122,22 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
   static int occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64], occ_c1p[64], occ_c2p[64];
   bool ok;
   if (wide)
-    ok = packed ? run_wide(P1(), PKT(), H, ub1, ev[0], ev[1])
-                : run_wide(P1(), PKF(), H, ub1, ev[0], ev[1]);
+    ok = packed ? run_wide(P1(), PKT(), H, ub1, ev[0], ev[1], claims1)
+                : run_wide(P1(), PKF(), H, ub1, ev[0], ev[1], claims1);
   else if (dt == CLE_BF16)
-    ok = packed ? run_phase(ffn_gemm_bf16<1, 4, 2, true, -1>, occ_c1p, 256, ub1, ev[0], ev[1])
-                : run_phase(ffn_gemm_bf16<1, 4, 2, false, -1>, occ_c1, 256, ub1, ev[0], ev[1]);
+    ok = packed ? run_phase(ffn_gemm_bf16<1, 4, 2, true, -1>, occ_c1p, 256, ub1, ev[0], ev[1], claims1)
+                : run_phase(ffn_gemm_bf16<1, 4, 2, false, -1>, occ_c1, 256, ub1, ev[0], ev[1], claims1);
   else
-    ok = run_phase(ffn_gemm_f32<1>, occ_f1, 256, ub1, ev[0], ev[1]);
+    ok = run_phase(ffn_gemm_f32<1>, occ_f1, 256, ub1, ev[0], ev[1], claims1);
   if (!ok) return CLE_EHIP;
   if (wide)
-    ok = packed ? run_wide(P2(), PKT(), I, ub2, ev[2], ev[3])
-                : run_wide(P2(), PKF(), I, ub2, ev[2], ev[3]);
+    ok = packed ? run_wide(P2(), PKT(), I, ub2, ev[2], ev[3], claims2)
+                : run_wide(P2(), PKF(), I, ub2, ev[2], ev[3], claims2);
   else if (dt == CLE_BF16)
-    ok = packed ? run_phase(ffn_gemm_bf16<2, 4, 2, true, -1>, occ_c2p, 256, ub2, ev[2], ev[3])
-                : run_phase(ffn_gemm_bf16<2, 4, 2, false, -1>, occ_c2, 256, ub2, ev[2], ev[3]);
+    ok = packed ? run_phase(ffn_gemm_bf16<2, 4, 2, true, -1>, occ_c2p, 256, ub2, ev[2], ev[3], claims2)
+                : run_phase(ffn_gemm_bf16<2, 4, 2, false, -1>, occ_c2, 256, ub2, ev[2], ev[3], claims2);
   else
-    ok = run_phase(ffn_gemm_f32<2>, occ_f2, 256, ub2, ev[2], ev[3]);
+    ok = run_phase(ffn_gemm_f32<2>, occ_f2, 256, ub2, ev[2], ev[3], claims2);
   if (!ok) return CLE_EHIP;
   return launch_status();
 }
