@@ -8,6 +8,12 @@ Pins (tests/test_oracle_engine.py):
   each micro-batch keeps its own layer order), by brute force over every
   path of the (l_0, l_1, l_2) state lattice of a tiny stack;
 * the per-layer baseline reproduces Eq. (3) computed layer by layer.
+Pins (tests/test_oracle_eq1.py):
+* moe_layer equals Eq. (1) of [PAPER] §2.1 evaluated token by token (brute
+  force top-k, torch's rms_norm / silu / linear per token, the residual from
+  the raw state), with and without the pre-norm block and shared experts;
+* run_engine, with the pre-norm block and with the router in front of top-k,
+  equals each token followed through every layer alone by that evaluation.
 """
 from __future__ import annotations
 
@@ -87,27 +93,44 @@ def run_schedule_only(w_table, n, L, D, m, policy, start_layers=None):
 
 
 def run_engine(h0, logits_fn, k, D, w13, w2, m, policy, w13s=None, w2s=None,
-               start_layers=None):
+               start_layers=None, prenorm=False, eps=1e-6, router=None):
     """Algorithm 1 with the full MoE math.
 
     h0: list of float64 [T_j, H]; logits_fn(j, l) -> float32 [T_j, E];
     w13 [L, E, 2I, H], w2 [L, E, H, I] float64 (shared: [L, S, ...]).
+    prenorm: the router and the experts read rmsnorm(h), the residual is h
+    (see moe_layer).  router: None (the logits are given by logits_fn), or
+    (w_gate [L, E, H], bias [L, E] | None) float64: a micro-batch is routed
+    from its current state, z = x W_g[l]^T + b[l] with x the block input
+    ([PAPER] §2.1, G(h'_l)), rounded to float32 as the top-k input.
     Returns (h_final list, trace, (num, den, sep), u).
     """
     n, L = len(h0), w13.shape[0]
     h = [np.array(x, dtype=np.float64) for x in h0]
     pending = {}
 
+    def scores(j, l):
+        if router is None:
+            return logits_fn(j, l)
+        x = moe.rmsnorm(h[j], eps) if prenorm else h[j]
+        wg, bias = router
+        return moe.gate_logits(x, wg[l], None if bias is None else bias[l]).astype(np.float32)
+
     def route_layer(j, l):
-        idx, _ = moe.route(logits_fn(j, l), k)
+        # AttnRouteDispatch: micro-batch j is at layer l and h[j] is that
+        # layer's input; its scores are kept for the layer's run
+        z = scores(j, l)
+        idx, _ = moe.route(z, k)
         counts, *_ = moe.dispatch(idx, w13.shape[1])
-        pending[j] = l
+        pending[j] = (l, z)
         return group_workload(counts, D)
 
     def run_layer(j, l):
-        assert pending[j] == l
-        out = moe_layer(h[j], logits_fn(j, l), k, w13[l], w2[l],
-                        None if w13s is None else w13s[l], None if w2s is None else w2s[l])
+        lp, z = pending[j]
+        assert lp == l
+        out = moe_layer(h[j], z, k, w13[l], w2[l],
+                        None if w13s is None else w13s[l], None if w2s is None else w2s[l],
+                        prenorm=prenorm, eps=eps)
         h[j] = out["y"]
 
     trace, steps_W, acc = _algorithm1(n, L, m, policy, start_layers, route_layer, run_layer)
