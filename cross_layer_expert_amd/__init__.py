@@ -99,6 +99,7 @@ _sig = {
                                       _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                       ctypes.POINTER(_vp), _vp]),
     "cle_pack_weights": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _vp]),
+    "cle_set_expert_tile": (_i32, [_i32]),
     "cle_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp]),
     "cle_workload_stats": (_i32, [_vp, _i32, _i32, _i32, _u64, _vp, _vp, _vp]),
     "cle_schedule_step": (_i32, [ctypes.POINTER(_i32), _i32, _i32, _u64, _i32, _i32,
@@ -253,6 +254,17 @@ def grouped_expert_ffn(descs, w13, w2, ws, w13_shared=None, w2_shared=None, even
         arr, len(descs), _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared), L, E, ns, H,
         I2 // 2, _dt(w13), W_PACKED if packed else W_ROWMAJOR, _ptr(ws),
         ws.numel() * ws.element_size(), ev, _stream(stream)))
+
+
+TILE_DEFAULT, TILE_128X256, TILE_256X256, TILE_128X512 = 0, 1, 2, 3
+TILES = {"default": 0, "128x256": 1, "256x256": 2, "128x512": 3}
+
+
+def set_expert_tile(tile):
+    """Output tile of the bf16 expert launches (process-wide; results are
+    bitwise the same for every tile): an int or a name of TILES."""
+    _check("cle_set_expert_tile", _lib.cle_set_expert_tile(TILES.get(tile, tile)
+                                                           if isinstance(tile, str) else tile))
 
 
 def pack_weights(src, dst=None, stream=None):

@@ -25,6 +25,8 @@
 // Consecutive logical tiles go to one XCD (workgroups are dealt round-robin
 // over the 8 XCDs) so tiles reading the same weight rows share that XCD's L2.
 #include <hip/hip_ext.h>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "cle_internal.h"
@@ -500,6 +502,10 @@ template <int PHASE, int WN, int NB, bool PACKED, int RH, int RG, int NMB, int T
           typename Hook = NoHook>
 __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane,
                                          const Hook& hook = Hook()) {
+  // lane-derived offsets (operand positions, epilogue rows) are recomputed per
+  // tile: hoisted out of the persistent loop they would hold a register each
+  // for the whole kernel
+  asm volatile("" : "+v"(lane));
   static_assert(WN * NB <= kBlocks && WN % RH == 0 && kMB % RH == 0, "weight blocks per tile");
   static_assert(NMB >= 0 && NMB <= kMB / RH && RG >= 0 && RG < RH, "row blocks per wavefront");
   constexpr int XB = kMB / WN;  // A row blocks loaded by each wavefront
@@ -693,19 +699,330 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane,
   }
 }
 
+// ---------------------------------------------------------------- 256-row tiles
+// The 8-wavefront tile with twice the rows: 256 rows x 256 weight rows.  Every
+// CU fetches its operands through its vector L1, whose outstanding misses are
+// limited, so on the large segments the rate at which a CU can bring operands
+// in (tens of bytes per clock, set by that limit and the L2 latency) rather
+// than the matrix cores sets the tile's time; this tile fetches (256 + 256) x K
+// operand elements per 256 x 256 x K products, two thirds of the 128-row
+// tile's bytes per FLOP.  A stage (K = 64) is 64 KiB, so the ring holds two:
+// stage k+2 is requested into stage k's buffer once every wavefront has read
+// stage k, and has the MFMAs of one stage to land.  K / 64 is even for every
+// shape this tile takes (K = H with H % 256 == 0, or K = I with I % 128 ==
+// 0), so the loop runs whole pairs of steps and needs no tail variants.  The
+// compute layout is the 128-row tile's 2 x 4 with 128 rows per row group.
+constexpr int kTM2 = 256;
+constexpr int kMB2 = kTM2 / 16;  // 16-row blocks per 256-row tile
+struct StageLDS2 {
+  uint4 w[kBlocks][2][64];  // [wave * 2 + block][row group][position]
+  uint4 x[kMB2][2][64];     // [row block][row group][position]
+};
+template <int PHASE, bool PACKED> __shared__ StageLDS2 g_sb0;
+template <int PHASE, bool PACKED> __shared__ StageLDS2 g_sb1;
+
+template <int PHASE, bool PACKED, int RG, int NMB, typename Hook = NoHook>
+__device__ __forceinline__ void tile256_nmb(const TileArgs& t, int wave, int lane,
+                                            const Hook& hook = Hook()) {
+  asm volatile("" : "+v"(lane));  // recomputed per tile, as in tile_nmb
+  constexpr int WN = 8, NB = 2, RH = 2;
+  constexpr int XB = kMB2 / WN;  // A row blocks loaded by each wavefront
+  constexpr int HB = NB / 2;
+  constexpr int RB = NB * RH;    // weight blocks each wavefront computes
+  constexpr int AM = NMB > 0 ? NMB : 1;
+  static_assert(NMB >= 0 && NMB <= kMB2 / RH && RG >= 0 && RG < RH, "row blocks per wavefront");
+  const int cg = wave % (WN / RH);
+  constexpr int xb0 = RG * (kMB2 / RH);  // first A row block of this wavefront
+  const int KT = t.K / kKS;
+  // load side: this lane fetches row lr of each 8-row group, chunk lc
+  const int lr = lane / 8, lc = (lane % 8) ^ (lane / 8);
+  const uint16_t* wp[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      wp[b][g] = (b < HB ? t.wlo : t.whi) + (b % HB) * 16 * t.K +
+                 (PACKED ? g * 512 + lane * 8 : (g * 8 + lr) * t.K + lc * 8);
+  const uint16_t* xp[XB][2];
+#pragma unroll
+  for (int b = 0; b < XB; ++b)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      // rows past the tile repeat its last row (never stored)
+      const int row = min((wave * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
+      const int64_t arow =
+          t.rmap ? static_cast<int64_t>(*(gcint*)(t.rmap + row) / t.kdiv) : row;
+      xp[b][g] = t.A + arow * t.K + lc * 8;
+    }
+  const int rg = (lane % 16) / 8, r8 = lane % 8;
+  const int pos0 = r8 * 8 + ((0 + lane / 16) ^ r8);
+  const int pos1 = r8 * 8 + ((4 + lane / 16) ^ r8);
+
+  f32x4 acc[RB][AM];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int mb = 0; mb < AM; ++mb) acc[b][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#define CLE_ISSUE(ST, KT_)                                                          \
+  {                                                                                 \
+    int kr = (KT_) + t.rot;                                                         \
+    kr -= kr >= KT ? KT : 0;                                                        \
+    const int ko = kr * kKS;                                                        \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
+      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
+        dma16(wp[b][g] + (PACKED ? kr * 1024 : ko), &ST.w[wave * NB + b][g][0]);     \
+    _Pragma("unroll") for (int b = 0; b < XB; ++b)                                  \
+      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
+        dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
+  }
+  bf16x8 fb[2][RB], fa[2][AM];
+#define CLE_READ(ST, H)                                                             \
+  if constexpr (NMB > 0) {                                                          \
+    const int pos = (H) == 0 ? pos0 : pos1;                                         \
+    _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
+      fb[H][b] = __builtin_bit_cast(bf16x8, ST.w[cg * RB + b][rg][pos]);            \
+    _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                              \
+      fa[H][mb] = __builtin_bit_cast(bf16x8, ST.x[xb0 + mb][rg][pos]);              \
+  }
+#define CLE_MFMA(H)                                                                 \
+  _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                                \
+    _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
+      acc[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[H][mb], fb[H][b], acc[b][mb], 0, 0, 0);
+  // Step KT_ (stage KT_ in CUR, KT_+1 in NXT): on entry the slice-0 MFMAs of
+  // stage KT_ are issued and its slice-1 operands are in registers.  Wait for
+  // this wavefront's loads of stage KT_+1 (the only ones in flight), barrier
+  // (every wavefront's loads of KT_+1 have landed and every wavefront has read
+  // all of CUR), request stage KT_+2 into CUR, then the slice-1 MFMAs of KT_
+  // while reading slice 0 of KT_+1, and the slice-0 MFMAs of KT_+1 while
+  // reading its slice 1.
+#define CLE_STEP2(CUR, NXT, KT_, ISS)                                               \
+  {                                                                                 \
+    wait_vmcnt<0>();                                                                \
+    stage_barrier();                                                                \
+    if constexpr (ISS) CLE_ISSUE(CUR, (KT_) + 2);                                   \
+    CLE_MFMA(1);                                                                    \
+    CLE_READ(NXT, 0);                                                               \
+    half_step_order<NMB, RB>();                                                     \
+    CLE_MFMA(0);                                                                    \
+    CLE_READ(NXT, 1);                                                               \
+    half_step_order<NMB, RB>();                                                     \
+  }
+  constexpr int kPerStep = 2 * NB + 2 * XB;
+  auto& sa = g_sb0<PHASE, PACKED>;
+  auto& sb = g_sb1<PHASE, PACKED>;
+  CLE_ISSUE(sa, 0);
+  CLE_ISSUE(sb, 1);
+  hook();
+  wait_vmcnt<kPerStep>();
+  stage_barrier();
+  CLE_READ(sa, 0);
+  CLE_MFMA(0);
+  CLE_READ(sa, 1);
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    CLE_STEP2(sa, sb, kt, true);
+    CLE_STEP2(sb, sa, kt + 1, true);
+  }
+  CLE_STEP2(sa, sb, kt, false);  // stage KT-2 in sa, KT-1 in sb
+  CLE_MFMA(1);                   // slice 1 of the last stage
+#undef CLE_ISSUE
+#undef CLE_READ
+#undef CLE_MFMA
+#undef CLE_STEP2
+  wait_vmcnt<0>();
+
+  const int g4 = lane / 16;
+  const int col = t.col + cg * RH * 16 * (PHASE == 1 ? HB : NB);
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (xb0 + mb) * 16 + g4 * 4 + i;
+      if (row < t.nrows) {
+        gu16* o = (gu16*)(t.out + row * t.ldo + col);
+        if (PHASE == 1) {
+#pragma unroll
+          for (int u = 0; u < RH; ++u)
+#pragma unroll
+            for (int b = 0; b < HB; ++b)
+              o[(u * HB + b) * 16] =
+                  bf16_hw(silu_hw(acc[u * NB + b][mb][i]) * acc[u * NB + HB + b][mb][i]);
+        } else {
+#pragma unroll
+          for (int b = 0; b < RB; ++b) o[b * 16] = bf16_hw(acc[b][mb][i]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------- 512-wide tiles
+// 128 rows x 512 weight rows (phase 1: 256 act columns, phase 2: 512 output
+// columns): each wavefront loads four weight blocks per stage.  What bounds
+// the expert launches on large segments is the traffic that misses L2 (the
+// MALL and HBM side sustains about 6.5 TB/s for the whole chip, L2 hits about
+// five times that): a segment's A rows are read once per column tile, and
+// concurrent tiles of one row tile start too far apart in time to share them
+// in L2, so A comes from HBM once per column tile.  Twice the columns per
+// tile halve those reads (3 instead of 6 column tiles at I = 768, 4 instead of
+// 8 at H = 2048).  A stage (K = 64) is 80 KiB, so the two stages fill the
+// LDS; the loop is the 256-row tile's (two stages, K / 64 even).  Compute
+// layout 1 x 8: each wavefront computes all 128 rows of the four weight
+// blocks it loaded itself.
+struct StageLDS4 {
+  uint4 w[32][2][64];   // [wave * 4 + block][row group][position]
+  uint4 x[kMB][2][64];  // [row block][row group][position]
+};
+template <int PHASE, bool PACKED> __shared__ StageLDS4 g_sw0;
+template <int PHASE, bool PACKED> __shared__ StageLDS4 g_sw1;
+
+template <int PHASE, bool PACKED, int NMB, typename Hook = NoHook>
+__device__ __forceinline__ void tile512_nmb(const TileArgs& t, int wave, int lane,
+                                            const Hook& hook = Hook()) {
+  asm volatile("" : "+v"(lane));  // recomputed per tile, as in tile_nmb
+  constexpr int WN = 8, NB = 4;
+  constexpr int XB = kMB / WN;  // one A row block loaded per wavefront
+  constexpr int HB = NB / 2;
+  constexpr int RB = NB;        // weight blocks each wavefront computes (its own)
+  constexpr int AM = NMB > 0 ? NMB : 1;
+  static_assert(NMB >= 1 && NMB <= kMB, "row blocks per wavefront");
+  const int KT = t.K / kKS;
+  const int lr = lane / 8, lc = (lane % 8) ^ (lane / 8);
+  const uint16_t* wp[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      wp[b][g] = (b < HB ? t.wlo : t.whi) + (b % HB) * 16 * t.K +
+                 (PACKED ? g * 512 + lane * 8 : (g * 8 + lr) * t.K + lc * 8);
+  const uint16_t* xp[XB][2];
+#pragma unroll
+  for (int b = 0; b < XB; ++b)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int row = min((wave * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
+      const int64_t arow =
+          t.rmap ? static_cast<int64_t>(*(gcint*)(t.rmap + row) / t.kdiv) : row;
+      xp[b][g] = t.A + arow * t.K + lc * 8;
+    }
+  const int rg = (lane % 16) / 8, r8 = lane % 8;
+  const int pos0 = r8 * 8 + ((0 + lane / 16) ^ r8);
+  const int pos1 = r8 * 8 + ((4 + lane / 16) ^ r8);
+
+  f32x4 acc[RB][AM];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int mb = 0; mb < AM; ++mb) acc[b][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#define CLE_ISSUE(ST, KT_)                                                          \
+  {                                                                                 \
+    int kr = (KT_) + t.rot;                                                         \
+    kr -= kr >= KT ? KT : 0;                                                        \
+    const int ko = kr * kKS;                                                        \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
+      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
+        dma16(wp[b][g] + (PACKED ? kr * 1024 : ko), &ST.w[wave * NB + b][g][0]);     \
+    _Pragma("unroll") for (int b = 0; b < XB; ++b)                                  \
+      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
+        dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
+  }
+  bf16x8 fb[2][RB], fa[2][AM];
+#define CLE_READ(ST, H)                                                             \
+  {                                                                                 \
+    const int pos = (H) == 0 ? pos0 : pos1;                                         \
+    _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
+      fb[H][b] = __builtin_bit_cast(bf16x8, ST.w[wave * NB + b][rg][pos]);          \
+    _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                              \
+      fa[H][mb] = __builtin_bit_cast(bf16x8, ST.x[mb][rg][pos]);                    \
+  }
+#define CLE_MFMA(H)                                                                 \
+  _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                                \
+    _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
+      acc[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[H][mb], fb[H][b], acc[b][mb], 0, 0, 0);
+#define CLE_STEP4(CUR, NXT, KT_, ISS)                                               \
+  {                                                                                 \
+    wait_vmcnt<0>();                                                                \
+    stage_barrier();                                                                \
+    if constexpr (ISS) CLE_ISSUE(CUR, (KT_) + 2);                                   \
+    CLE_MFMA(1);                                                                    \
+    CLE_READ(NXT, 0);                                                               \
+    half_step_order<NMB, RB>();                                                     \
+    CLE_MFMA(0);                                                                    \
+    CLE_READ(NXT, 1);                                                               \
+    half_step_order<NMB, RB>();                                                     \
+  }
+  constexpr int kPerStep = 2 * NB + 2 * XB;
+  auto& sa = g_sw0<PHASE, PACKED>;
+  auto& sb = g_sw1<PHASE, PACKED>;
+  CLE_ISSUE(sa, 0);
+  CLE_ISSUE(sb, 1);
+  hook();
+  wait_vmcnt<kPerStep>();
+  stage_barrier();
+  CLE_READ(sa, 0);
+  CLE_MFMA(0);
+  CLE_READ(sa, 1);
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    CLE_STEP4(sa, sb, kt, true);
+    CLE_STEP4(sb, sa, kt + 1, true);
+  }
+  CLE_STEP4(sa, sb, kt, false);  // stage KT-2 in sa, KT-1 in sb
+  CLE_MFMA(1);
+#undef CLE_ISSUE
+#undef CLE_READ
+#undef CLE_MFMA
+#undef CLE_STEP4
+  wait_vmcnt<0>();
+
+  // lane holds rows mb*16 + (lane/16)*4 + i, column lane%16 of each of its
+  // blocks; phase 1 pairs gate block b with up block HB + b (act columns of
+  // consecutive pairs 16 apart)
+  const int g4 = lane / 16;
+  const int col = t.col + wave * 16 * (PHASE == 1 ? HB : NB);
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = mb * 16 + g4 * 4 + i;
+      if (row < t.nrows) {
+        gu16* o = (gu16*)(t.out + row * t.ldo + col);
+        if (PHASE == 1) {
+#pragma unroll
+          for (int b = 0; b < HB; ++b)
+            o[b * 16] = bf16_hw(silu_hw(acc[b][mb][i]) * acc[HB + b][mb][i]);
+        } else {
+#pragma unroll
+          for (int b = 0; b < RB; ++b) o[b * 16] = bf16_hw(acc[b][mb][i]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int PHASE, int WN, int NB, bool PACKED, int TM> __shared__ int g_snext[2][4];
+
 // Tiles go to XCDs in contiguous ranges of ceil(total / 8); within its XCD's
 // range a workgroup takes the tile at (range start + its index among the XCD's
 // workgroups) first, and then whichever tile the XCD's claim counter hands it,
 // so the workgroups of an XCD finish within about one tile of each other
 // whatever the tiles' lengths.  claims: this phase's 8 counters, zeroed by the
 // planner.
-template <int PHASE, int WN, int NB, bool PACKED, int TR>
+template <int PHASE, int WN, int NB, bool PACKED, int TR, int TM = kTM>
 __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restrict__ segs,
                                                             int nseg,
                                                             const int* __restrict__ totals,
                                                             int* __restrict__ claims,
                                                             Weights wts, int H, int I) {
-  static_assert(kMB % WN == 0 && WN * NB <= kBlocks && NB % 2 == 0, "tile shape");
+  constexpr bool kWide4 = NB == 4;  // the 512-wide tile (its stages fill the LDS)
+  static_assert(kMB % WN == 0 && (WN * NB <= kBlocks || (kWide4 && WN == 8 && TM == kTM)) &&
+                    NB % 2 == 0, "tile shape");
+  static_assert(TM == kTM || (TM == kTM2 && WN == 8 && NB == 2), "tile height");
+  constexpr int MBT = TM / 16;  // 16-row blocks per tile
   constexpr int HB = NB / 2;
   constexpr int RH = WN == 8 ? 2 : 1;  // row groups of the compute layout
   const int total = totals[PHASE - 1];
@@ -722,9 +1039,11 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
   const int xcd = blockIdx.x % kXcds, chunk = grid / kXcds;
   const int per = (total + kXcds - 1) / kXcds;
   const int lo = min(total, xcd * per), hi = min(total, lo + per);
-  __shared__ int s_next[2][4];  // by tile parity: next tile and its position
+  // by tile parity: next tile and its position (the 512-wide tile hands them
+  // over through its stage buffer instead)
+  auto& s_next = g_snext<PHASE, WN, NB, PACKED, TM>;
   int tile = lo + static_cast<int>(blockIdx.x) / kXcds;
-  TilePos next = tile < hi ? locate_tile(segs, nseg, tile, ncols, kTM) : TilePos{0, 0, 0};
+  TilePos next = tile < hi ? locate_tile(segs, nseg, tile, ncols, TM) : TilePos{0, 0, 0};
   for (int par = 0; tile < hi; par ^= 1) {
     const TilePos tp = next;
     // Wavefront 0 claims the workgroup's next tile before this tile's first
@@ -743,8 +1062,8 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     const auto look_ahead = [&]() {
       if (wave == 0) {
         tnext = lo + chunk + __builtin_amdgcn_readfirstlane(claim);
-        if (tnext < hi) next = locate_tile(segs, nseg, tnext, ncols, kTM);
-        if (lane == 0) {
+        if (tnext < hi) next = locate_tile(segs, nseg, tnext, ncols, TM);
+        if (!kWide4 && lane == 0) {
           s_next[par][0] = tnext;
           s_next[par][1] = next.si;
           s_next[par][2] = next.nt;
@@ -754,7 +1073,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     };
     const Seg sg = segs[tp.si];
     const int nt = tp.nt, mi = tp.mi;
-    const int row0 = mi * kTM;
+    const int row0 = mi * TM;
     TileArgs t;
     t.K = K;
     // kdiv and kkey read as one 32-bit word (scalar load; see locate_tile)
@@ -762,7 +1081,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     __builtin_memcpy(&kw, &segs[tp.si].kdiv, sizeof(kw));
     const int kdiv = static_cast<int16_t>(kw & 0xffff), kkey = (kw >> 16) & 0xffff;
     t.rot = kkey % (K / kKS);
-    t.nrows = min(kTM, sg.rows - row0);
+    t.nrows = min(TM, sg.rows - row0);
     // The output row stride is laundered per tile: otherwise the compiler
     // hoists every per-row output offset (row * stride, one register per
     // row) out of the tile loop and keeps them all live.
@@ -797,8 +1116,47 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     t.whi = W + static_cast<int64_t>(whi) * K;
     // row blocks this wavefront computes: its row group's share of the tile
     const int rg = wave / (WN / RH);
-    const int nmb = min(max((t.nrows + 15) / 16 - rg * (kMB / RH), 0), kMB / RH);
-    if constexpr (RH == 2) {
+    const int nmb = min(max((t.nrows + 15) / 16 - rg * (MBT / RH), 0), MBT / RH);
+    if constexpr (kWide4) {
+      const int nall = (t.nrows + 15) / 16;
+      switch (nall) {
+        case 1: tile512_nmb<PHASE, PACKED, 1>(t, wave, lane, look_ahead); break;
+        case 2: tile512_nmb<PHASE, PACKED, 2>(t, wave, lane, look_ahead); break;
+        case 3: tile512_nmb<PHASE, PACKED, 3>(t, wave, lane, look_ahead); break;
+        case 4: tile512_nmb<PHASE, PACKED, 4>(t, wave, lane, look_ahead); break;
+        case 5: tile512_nmb<PHASE, PACKED, 5>(t, wave, lane, look_ahead); break;
+        case 6: tile512_nmb<PHASE, PACKED, 6>(t, wave, lane, look_ahead); break;
+        case 7: tile512_nmb<PHASE, PACKED, 7>(t, wave, lane, look_ahead); break;
+        default: tile512_nmb<PHASE, PACKED, 8>(t, wave, lane, look_ahead); break;
+      }
+    } else if constexpr (TM == kTM2) {
+#define CLE_T2(RG_, N_) tile256_nmb<PHASE, PACKED, RG_, N_>(t, wave, lane, look_ahead)
+      if (rg == 0) {
+        switch (nmb) {
+          case 1: CLE_T2(0, 1); break;
+          case 2: CLE_T2(0, 2); break;
+          case 3: CLE_T2(0, 3); break;
+          case 4: CLE_T2(0, 4); break;
+          case 5: CLE_T2(0, 5); break;
+          case 6: CLE_T2(0, 6); break;
+          case 7: CLE_T2(0, 7); break;
+          default: CLE_T2(0, 8); break;
+        }
+      } else {
+        switch (nmb) {
+          case 0: CLE_T2(1, 0); break;
+          case 1: CLE_T2(1, 1); break;
+          case 2: CLE_T2(1, 2); break;
+          case 3: CLE_T2(1, 3); break;
+          case 4: CLE_T2(1, 4); break;
+          case 5: CLE_T2(1, 5); break;
+          case 6: CLE_T2(1, 6); break;
+          case 7: CLE_T2(1, 7); break;
+          default: CLE_T2(1, 8); break;
+        }
+      }
+#undef CLE_T2
+    } else if constexpr (RH == 2) {
       if (rg == 0) {
         switch (nmb) {
           case 1: tile_nmb<PHASE, WN, NB, PACKED, RH, 0, 1, TR>(t, wave, lane, look_ahead); break;
@@ -830,7 +1188,23 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     // every wavefront is done reading the stages before the next tile's
     // first requests overwrite them
     stage_barrier();
-    if (wave != 0) {
+    if constexpr (kWide4) {
+      // wavefront 0 leaves the next tile in stage 1's buffer; every wavefront
+      // has read it before the next tile requests stage 1 there
+      uint4* hand = &g_sw1<PHASE, PACKED>.x[0][0][0];
+      if (wave == 0 && lane == 0)
+        *hand = make_uint4(static_cast<unsigned>(tnext), static_cast<unsigned>(next.si),
+                           static_cast<unsigned>(next.nt), static_cast<unsigned>(next.mi));
+      stage_barrier();
+      if (wave != 0) {
+        const uint4 v = *hand;
+        tnext = __builtin_amdgcn_readfirstlane(static_cast<int>(v.x));
+        next = TilePos{__builtin_amdgcn_readfirstlane(static_cast<int>(v.y)),
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(v.z)),
+                       __builtin_amdgcn_readfirstlane(static_cast<int>(v.w))};
+      }
+      stage_barrier();
+    } else if (wave != 0) {
       tnext = s_next[par][0];
       next = TilePos{s_next[par][1], s_next[par][2], s_next[par][3]};
     }
@@ -976,6 +1350,22 @@ int resident_blocks(Kernel kernel, int* cache, int threads) {
   return cache[dev];
 }
 
+// Tile of the 8-wavefront bf16 kernels (cle_set_expert_tile): an explicit
+// choice, else the environment's CLE_TILE read once, else 128 x 256.
+enum WideTile { kTile128x256 = CLE_TILE_128X256, kTile256x256 = CLE_TILE_256X256,
+                kTile128x512 = CLE_TILE_128X512 };
+int g_tile_choice = CLE_TILE_DEFAULT;
+
+WideTile wide_tile_shape() {
+  static const WideTile env = [] {
+    const char* v = getenv("CLE_TILE");
+    if (v && !strcmp(v, "256x256")) return kTile256x256;
+    if (v && !strcmp(v, "128x512")) return kTile128x512;
+    return kTile128x256;
+  }();
+  return g_tile_choice == CLE_TILE_DEFAULT ? env : static_cast<WideTile>(g_tile_choice);
+}
+
 int persistent_grid(int64_t upper_bound_tiles, int resident) {
   int64_t g = resident;
   if (upper_bound_tiles < g) g = upper_bound_tiles;
@@ -985,6 +1375,12 @@ int persistent_grid(int64_t upper_bound_tiles, int resident) {
 
 }  // namespace
 }  // namespace cle
+
+extern "C" cle_status cle_set_expert_tile(int32_t tile) {
+  if (tile < CLE_TILE_DEFAULT || tile > CLE_TILE_128X512) return CLE_EINVAL;
+  cle::g_tile_choice = tile;
+  return CLE_OK;
+}
 
 extern "C" cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_desc,
                                              const void* w13, const void* w2,
@@ -1016,9 +1412,11 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
   if (I < 64 || I % 64) return CLE_EINVAL;
   if (dt == CLE_BF16 ? (H < 128 || H % 128) : (H < 64 || H % 64)) return CLE_EINVAL;
   const bool wide = dt == CLE_BF16 && I % 128 == 0 && H % 256 == 0;
-  const int tm = dt == CLE_BF16 ? kTM : kBM;
-  const int tn1 = dt == CLE_BF16 ? (wide ? 128 : 64) : kBNF;
-  const int tn2 = dt == CLE_BF16 ? (wide ? 256 : 128) : kBNF;
+  const bool tall = wide && wide_tile_shape() == kTile256x256;
+  const bool wide4 = wide && wide_tile_shape() == kTile128x512 && I % 256 == 0 && H % 512 == 0;
+  const int tm = dt == CLE_BF16 ? (tall ? kTM2 : kTM) : kBM;
+  const int tn1 = dt == CLE_BF16 ? (wide4 ? 256 : wide ? 128 : 64) : kBNF;
+  const int tn2 = dt == CLE_BF16 ? (wide4 ? 512 : wide ? 256 : 128) : kBNF;
   if (n_shared > 0 && (!w13_shared || !w2_shared)) return CLE_EINVAL;
   const int esz = dt == CLE_BF16 ? 2 : 4;
   if (!aligned(w13, 16) || !aligned(w2, 16)) return CLE_EINVAL;
@@ -1106,7 +1504,10 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
                       int* claims) {
     constexpr int P = decltype(phase)::value;
     constexpr bool PK = decltype(pk)::value;
-    static int occ_t2[64], occ_t3[64], occ_t4[64], occ_any[64];
+    static int occ_t2[64], occ_t3[64], occ_t4[64], occ_any[64], occ_256[64];
+    static int occ_512[64];
+    if (tall) return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 0, kTM2>, occ_256, 512, ub, e0, e1, claims);
+    if (wide4) return run_phase(ffn_gemm_bf16<P, 8, 4, PK, 0>, occ_512, 512, ub, e0, e1, claims);
     const int kt = K / kKS;
     switch (kt >= 3 ? 2 + (kt - 3) % 3 : -1) {
       case 2: return run_phase(ffn_gemm_bf16<P, 8, 2, PK, 2>, occ_t2, 512, ub, e0, e1, claims);

@@ -201,6 +201,29 @@ cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_desc,
                                   void* const* phase_events, void* stream);
 
 /*
+ * cle_set_expert_tile -- the output tile of the bf16 expert launches
+ * (process-wide; takes effect at the next cle_grouped_expert_ffn or
+ * cle_loop_step call).  A tuning choice only: the results are bitwise the
+ * same for every tile, since each output element is the same sequence of
+ * MFMAs over the same K order.
+ *   CLE_TILE_DEFAULT  (0) the library's default (CLE_TILE_128X256, or the
+ *                     shape named by the environment variable CLE_TILE,
+ *                     "128x256" / "256x256" / "128x512", when it is set);
+ *   CLE_TILE_128X256  (1) 128 rows x 256 weight rows;
+ *   CLE_TILE_256X256  (2) 256 rows x 256 weight rows;
+ *   CLE_TILE_128X512  (3) 128 rows x 512 weight rows, used where I % 256 == 0
+ *                     and H % 512 == 0 (otherwise 128 x 256).
+ * The 8-wavefront tiles need I % 128 == 0 and H % 256 == 0; other shapes use
+ * 128 x 128 tiles whatever the setting.  Not synchronised with launches in
+ * flight on other host threads.  Returns CLE_EINVAL for an unknown value.
+ */
+#define CLE_TILE_DEFAULT 0
+#define CLE_TILE_128X256 1
+#define CLE_TILE_256X256 2
+#define CLE_TILE_128X512 3
+cle_status cle_set_expert_tile(int32_t tile);
+
+/*
  * cle_pack_weights -- re-lays out n_mat row-major bf16 matrices [R, K] (src)
  * into the CLE_W_PACKED layout (dst, same size, must not overlap src), for
  * cle_grouped_expert_ffn with w_layout = CLE_W_PACKED.  Pack each of w13

@@ -3,7 +3,7 @@ cle_combine_many) against the oracle and against the per-micro-batch calls.
 
 Bars: indices, dispatch outputs and combine outputs bit-exact with the
 per-micro-batch calls (same kernels, one launch); routing and dispatch
-bit-exact with the oracle, gates within the documented 1-ulp allowance; the
+bit-exact with the oracle, gates included; the
 batched engine bitwise equal to the per-micro-batch engine over whole runs.
 """
 import numpy as np
@@ -14,7 +14,7 @@ import cross_layer_expert_amd as cle
 import oracle
 import synth
 from cross_layer_expert_amd.engine import Engine
-from gpu_helpers import bits_of, device, f32_ulp_diff, to_dev
+from gpu_helpers import bits_of, device, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -47,8 +47,7 @@ def test_route_many(n, T, E, k):
     for j in range(n):
         ridx, rgate = oracle.route(z[j], k)
         assert np.array_equal(idx[j].cpu().numpy(), ridx), j
-        u = f32_ulp_diff(gate[j].cpu().numpy(), rgate)
-        assert u.max() <= 1 and (u > 0).sum() <= max(1, u.size // 10000), j
+        assert np.array_equal(gate[j].cpu().numpy().view(np.int32), rgate.view(np.int32)), j
 
 
 @pytest.mark.parametrize("n,T,k,E,skew", [(3, 2048, 8, 128, 1.1), (64, 7, 3, 16, 2.0),

@@ -42,18 +42,22 @@ def _tiny_setup(seed=0):
 
 @pytest.mark.parametrize("policy", ["b0", "b1", "cumutil", "maxutil", "diffpeak"])
 @pytest.mark.parametrize("m", [1, 2, 3])
-def test_tiny_engine_matches_oracle(policy, m):
+@pytest.mark.parametrize("prenorm", [False, True])
+def test_tiny_engine_matches_oracle(policy, m, prenorm):
     (W, logits_t, h0_t), (w13, w2, logits, h0) = _tiny_setup()
-    eng = Engine(W, logits_t, h0_t, TINY.D, TINY.k, cle.POLICIES[policy], m).run()
+    eng = Engine(W, logits_t, h0_t, TINY.D, TINY.k, cle.POLICIES[policy], m,
+                 prenorm=prenorm).run()
     torch.cuda.synchronize()
     h_ref, trace, acc, u = oracle.run_engine(h0, lambda j, l: logits[j, l], TINY.k, TINY.D,
-                                             w13, w2, m, oracle.POLICIES[policy])
+                                             w13, w2, m, oracle.POLICIES[policy],
+                                             prenorm=prenorm, eps=cle.NORM_EPS)
     assert eng.trace == trace, "schedule differs from the oracle's Algorithm 1"
     a, ug = eng.stats()
     assert a[:3] == list(acc) and a[3] == len(trace)
     assert abs(ug - float(u)) < 1e-12
     for j in range(TINY.n):
-        check_close(to_host(eng.h[j]), h_ref[j], 1e-5, 1e-5, what=f"h[{j}] {policy} m={m}")
+        check_close(to_host(eng.h[j]), h_ref[j], 1e-5, 1e-5,
+                    what=f"h[{j}] {policy} m={m} prenorm={prenorm}")
 
 
 def test_tiny_state_lattice_bitwise():

@@ -3,16 +3,23 @@
 One cross-layer step with every micro-batch at a different layer (the hidden
 states at those layers are seeded inputs, so the oracle needs nothing from
 the GPU):
-  * routing indices and dispatch permutation: bit-exact, every token;
+  * routing indices, gates and the dispatch permutation: bit-exact, every
+    token;
   * workloads and step statistics: exact;
-  * expert outputs of sampled segments (hottest, median, smallest non-empty)
-    and combined outputs of sampled tokens: max-abs 2e-2, normwise 1e-2;
-and for the Qwen3-shaped stack the whole cross-layer run (device-driven) is bitwise equal
-to the run with one (micro-batch, layer) per step, with finite hidden states
-after all 48 layers.  Launch configuration of bench.py: packed weights,
-pre-norm block (the experts read the RMS-normalised rows, compared here from
-the GPU's own bf16 normalised rows after checking those against the oracle's
-normalisation), device-driven step.
+  * expert outputs of every segment (and of the shared experts): within the
+    element-wise rounding-error bound of the float64 oracle
+    (gpu_helpers.swiglu_bound) and within the workload's tolerance for expert
+    outputs (max-abs 2e-2, normwise 1e-2);
+  * the layer output of every token: within the element-wise bound carried
+    through the combine, and normwise 1e-2 (its values reach 4-6, where half
+    a bf16 ulp alone is 2^-6, so the absolute bar does not apply);
+for the Qwen3-, Moonlight-, task-shift-, decode- and long-prefill-shaped
+stacks.  For the Qwen3-shaped stack the whole cross-layer run (device-driven)
+is also bitwise equal to the run with one (micro-batch, layer) per step,
+with finite hidden states after all 48 layers.  Launch configuration of
+bench.py: packed weights, pre-norm block (the experts read the
+RMS-normalised rows, compared here from the GPU's own bf16 normalised rows
+after checking those against the oracle's normalisation), device-driven step.
 """
 import gc
 
@@ -24,11 +31,13 @@ import cross_layer_expert_amd as cle
 import oracle
 import synth
 from cross_layer_expert_amd.engine import Engine
-from gpu_helpers import bits_of, check_close, device, f32_ulp_diff, to_dev, to_host
+from gpu_helpers import (LAM, U32, bits_of, check_bound, check_close, device, swiglu_bound,
+                         to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
 TOL = (2e-2, 1e-2)
+UB = 2.0 ** -8   # bf16 unit roundoff
 
 
 def _w(t):
@@ -70,8 +79,8 @@ def _one_cross_layer_step(name, start):
         z = logits[j, l]
         ridx, rg = oracle.route(z, cfg.k)
         assert np.array_equal(eng.idx[j].cpu().numpy(), ridx), f"route idx j={j}"
-        u = f32_ulp_diff(eng.gates[j].cpu().numpy(), rg)
-        assert u.max() <= 1 and (u > 0).sum() <= max(1, u.size // 10000), f"gates j={j}"
+        assert np.array_equal(eng.gates[j].cpu().numpy().view(np.int32), rg.view(np.int32)), \
+            f"gates j={j}"
         counts, offsets, dest, src = oracle.dispatch(ridx, cfg.E)
         assert np.array_equal(eng.counts[j].cpu().numpy(), counts)
         assert np.array_equal(eng.offsets[j].cpu().numpy(), offsets)
@@ -84,29 +93,52 @@ def _one_cross_layer_step(name, start):
         xn = oracle.widen(to_host(eng.xn[j]), "bf16")
         rn = oracle.rmsnorm(x, cle.NORM_EPS)
         assert np.all(np.abs(xn - rn) <= (2.0 ** -8 + 1e-5) * np.abs(rn) + 1e-30)
-        # sampled segments: hottest, median non-empty, smallest non-empty
-        nz = np.flatnonzero(counts)
-        order = nz[np.argsort(counts[nz], kind="stable")]
-        for e in sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])}):
+        # every segment of the expert-sorted rows
+        A = cfg.T * cfg.k
+        got_yp = oracle.widen(to_host(eng.yp[j][:A]), "bf16")
+        ref_yp = np.zeros((A, cfg.H))
+        bnd_yp = np.zeros((A, cfg.H))
+        worst = 0.0
+        for e in np.flatnonzero(counts):
             a, b = int(offsets[e]), int(offsets[e + 1])
             xs = xn[src[a:b] // cfg.k]
-            ref = oracle.swiglu_expert(xs, _w(w13[l, e]), _w(w2[l, e]))
-            got = oracle.widen(to_host(eng.yp[j][a:b]), "bf16")
-            check_close(got, ref, *TOL, what=f"{name} j={j} l={l} e={e} rows={b - a}")
-        # sampled tokens: the full layer output of one token from inputs only
-        rng = np.random.default_rng(j)
-        for t in rng.choice(cfg.T, 3, replace=False):
-            xt = xn[t:t + 1]
-            yp = np.concatenate([oracle.swiglu_expert(xt, _w(w13[l, int(e)]), _w(w2[l, int(e)]))
-                                 for e in ridx[t]])
-            ysh = None
-            if cfg.n_shared:
-                ysh = [oracle.swiglu_expert(xt, _w(w13s[l, q]), _w(w2s[l, q]))
-                       for q in range(cfg.n_shared)]
-            ref = oracle.combine(yp, np.arange(cfg.k), rg[t:t + 1], cfg.k, y_shared=ysh,
-                                 residual=x[t:t + 1])
-            got = oracle.widen(to_host(eng.h[j][t:t + 1]), "bf16")
-            check_close(got, ref, *TOL, what=f"{name} j={j} token {t}")
+            we13, we2 = _w(w13[l, e]), _w(w2[l, e])
+            ref_yp[a:b] = oracle.swiglu_expert(xs, we13, we2)
+            bnd_yp[a:b] = swiglu_bound(xs, we13, we2, "bf16")
+            worst = max(worst, check_bound(got_yp[a:b], ref_yp[a:b], bnd_yp[a:b], quiet=True,
+                                           what=f"{name} j={j} l={l} e={int(e)} rows={b - a}"))
+        print(f"[bound] {name} j={j} l={l}: {np.count_nonzero(counts)} segments, "
+              f"max |err|/bound = {worst:.3f}", flush=True)
+        check_close(got_yp, ref_yp, *TOL, what=f"{name} j={j} all expert rows")
+        ref_sh, bnd_sh = None, 0.0
+        if cfg.n_shared:
+            ref_sh = []
+            got_sh = oracle.widen(to_host(eng.y_sh[j]), "bf16")
+            for q in range(cfg.n_shared):
+                ws13, ws2 = _w(w13s[l, q]), _w(w2s[l, q])
+                r = oracle.swiglu_expert(xn, ws13, ws2)
+                bq = swiglu_bound(xn, ws13, ws2, "bf16")
+                check_bound(got_sh[q], r, bq, what=f"{name} j={j} shared {q}")
+                check_close(got_sh[q], r, *TOL, what=f"{name} j={j} shared {q}")
+                ref_sh.append(r)
+                bnd_sh = bnd_sh + bq
+        # every token's layer output (Eq. (1) + shared experts + residual)
+        ref = oracle.combine(ref_yp, dest, rg, cfg.k, y_shared=ref_sh, residual=x)
+        g = rg.astype(np.float64)
+        dk = dest.reshape(cfg.T, cfg.k)
+        carried = sum(g[:, s:s + 1] * bnd_yp[dk[:, s]] for s in range(cfg.k)) + bnd_sh
+        mag = sum(g[:, s:s + 1] * np.abs(ref_yp[dk[:, s]]) for s in range(cfg.k)) + np.abs(x)
+        if ref_sh is not None:
+            mag = mag + sum(np.abs(r) for r in ref_sh)
+        nterms = cfg.k + cfg.n_shared + 1
+        bound = UB * np.abs(ref) + carried + LAM * np.sqrt(nterms) * U32 * mag + 1e-30
+        got = oracle.widen(to_host(eng.h[j]), "bf16")
+        check_bound(got, ref, bound, what=f"{name} j={j} every token")
+        # the layer outputs reach |y| ~ 4-6 (the residual), where half an ulp of
+        # bf16 is already 2^-6: the absolute 2e-2 bar, stated for expert
+        # outputs, is below the output format's resolution there, so layer
+        # outputs take the element-wise bound and the normwise bar
+        check_close(got, ref, np.inf, TOL[1], what=f"{name} j={j} all tokens")
     # statistics of the step (B1: every micro-batch in one step)
     acc, _ = eng.stats()
     a, b, c = oracle.step_stats(wrows)
@@ -122,6 +154,11 @@ def test_qwen3_cross_layer_step():
 
 def test_moonlight_cross_layer_step():
     _one_cross_layer_step("moonlight", [0, 3, 7, 10, 14, 18, 21, 25])
+
+
+def test_taskshift_cross_layer_step():
+    """Six micro-batches drawn from three skew profiles, each at its own layer."""
+    _one_cross_layer_step("taskshift", [0, 9, 18, 27, 36, 47])
 
 
 def test_decode_staggered_step():

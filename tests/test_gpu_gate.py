@@ -7,7 +7,7 @@ Bars:
   in float32; only the sum rounds), and bitwise reproducible, batched equal
   to per-micro-batch, packed equal to row-major;
 * routing of the GPU logits bit-exact with the oracle's routing of the same
-  logits (indices; gates within the 1-ulp allowance of the route kernel);
+  logits (indices and gates);
 * the selection valid against the oracle logits up to twice the bound
   (near-ties may flip: several answers are correct, so validity is checked);
 * device-driven runs routed through the gate bitwise equal to host-driven.
@@ -20,7 +20,7 @@ import cross_layer_expert_amd as cle
 import oracle
 import synth
 from cross_layer_expert_amd.engine import Engine
-from gpu_helpers import bits_of, device, f32_ulp_diff, to_dev, to_host
+from gpu_helpers import bits_of, device, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -97,8 +97,7 @@ def test_gate_logits_and_routing(n, T, H, E, k, dtype, use_bias, packed):
         assert np.all(err <= bound)
         flips = _check_routing(zg, ref, bound, idx[j].cpu().numpy(), k)
         _, rg = oracle.route(zg, k)
-        u = f32_ulp_diff(gate[j].cpu().numpy(), rg)
-        assert u.max() <= 1 and (u > 0).sum() <= max(1, u.size // 10000)
+        assert np.array_equal(gate[j].cpu().numpy().view(np.int32), rg.view(np.int32))
         print(f"[gate] j={j} tokens whose top-k set differs from the exact logits': {flips}",
               flush=True)
 

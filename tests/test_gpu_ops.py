@@ -2,11 +2,11 @@
 C ABI, on seeded inputs that span several tiles, ragged tails and the
 degenerate cases of the method.
 
-Bars: routing indices, dispatch outputs, workloads and statistics are
-bit-exact; gates are bit-exact up to the documented 1-ulp allowance (float64
-exp is not correctly rounded on either side); bf16 expert outputs are within
-max-abs 2e-2 and normwise relative 1e-2 of the float64 oracle; float32 paths
-within 1e-5.
+Bars: routing indices, gates, dispatch outputs, workloads and statistics
+are bit-exact; expert outputs are within the element-wise rounding-error
+bound of the expert FFN (gpu_helpers.swiglu_bound) of the float64 oracle,
+and bf16 ones also within max-abs 2e-2 and normwise relative 1e-2 (the
+workload's stated tolerance); float32 paths also within 1e-5.
 """
 import numpy as np
 import pytest
@@ -15,7 +15,8 @@ import torch
 import cross_layer_expert_amd as cle
 import oracle
 import synth
-from gpu_helpers import bits_of, check_close, device, f32_ulp_diff, to_dev, to_host
+from gpu_helpers import (bits_of, check_bound, check_close, device, f32_ulp_diff,
+                         swiglu_bound, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +40,7 @@ def _route_case(z, k):
     nbad = int((ulps > 0).sum())
     print(f"[route] T={T} E={E} k={k}: gate mismatches {nbad}/{gg.size}, max ulp {ulps.max()}",
           flush=True)
-    assert ulps.max() <= 1 and nbad <= max(1, gg.size // 10000)
+    assert np.array_equal(gg.view(np.int32), rgate.view(np.int32)), "gates differ (bits)"
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen3", "moonlight", "taskshift"])
@@ -267,14 +268,21 @@ def _ffn_case(dtype, H, I, E, L, ns, layers, sizes_list, seed=0, T_shared=None):
         descs.append(cle.make_desc(l, rows, t["offsets"], t["xp"], t["act"], t["yp"],
                                    Ts if ns else 0, t.get("xs"), t.get("acts"), t.get("ys")))
         x64 = oracle.widen(xp, dtype)
-        ref_y = oracle.expert_ffn(x64, offsets, oracle.widen(w13[l], dtype),
-                                  oracle.widen(w2[l], dtype))
-        ref_sh = None
+        w13l, w2l = oracle.widen(w13[l], dtype), oracle.widen(w2[l], dtype)
+        ref_y = oracle.expert_ffn(x64, offsets, w13l, w2l)
+        bnd_y = np.zeros_like(ref_y)
+        for e in range(E):
+            a, b = int(offsets[e]), int(offsets[e + 1])
+            if b > a:
+                bnd_y[a:b] = swiglu_bound(x64[a:b], w13l[e], w2l[e], dtype)
+        ref_sh = bnd_sh = None
         if ns:
             xs64 = oracle.widen(xs, dtype)
-            ref_sh = [oracle.swiglu_expert(xs64, oracle.widen(w13s[l, q], dtype),
-                                           oracle.widen(w2s[l, q], dtype)) for q in range(ns)]
-        refs.append((ref_y, ref_sh, rows))
+            pairs = [(oracle.widen(w13s[l, q], dtype), oracle.widen(w2s[l, q], dtype))
+                     for q in range(ns)]
+            ref_sh = [oracle.swiglu_expert(xs64, a13, a2) for a13, a2 in pairs]
+            bnd_sh = [swiglu_bound(xs64, a13, a2, dtype) for a13, a2 in pairs]
+        refs.append((ref_y, ref_sh, rows, bnd_y, bnd_sh))
     ws = torch.empty(cle.workspace_bytes(cle.OP_FFN, 0, E, 1, ns, len(descs)) // 4,
                      dtype=torch.int32, device=dev)
     return dict(descs=descs, keep=keep, refs=refs, W=(W13, W2, W13s, W2s), ws=ws, dtype=dtype)
@@ -290,12 +298,15 @@ def _run_ffn(case, which=None):
 def _check_ffn(case):
     dtype = case["dtype"]
     tol = (BF16_MAX_ABS, BF16_REL) if dtype == "bf16" else (F32_TOL, F32_TOL)
-    for j, (t, (ref_y, ref_sh, rows)) in enumerate(zip(case["keep"], case["refs"])):
+    for j, (t, (ref_y, ref_sh, rows, bnd_y, bnd_sh)) in enumerate(zip(case["keep"],
+                                                                      case["refs"])):
         got = oracle.widen(to_host(t["yp"])[:rows], dtype)
+        check_bound(got, ref_y, bnd_y, what=f"yp[{j}]")
         check_close(got, ref_y, *tol, what=f"yp[{j}]")
         if ref_sh is not None:
             gs = oracle.widen(to_host(t["ys"]), dtype)
             for q, r in enumerate(ref_sh):
+                check_bound(gs[q], r, bnd_sh[q], what=f"y_shared[{j},{q}]")
                 check_close(gs[q], r, *tol, what=f"y_shared[{j},{q}]")
 
 
@@ -419,9 +430,14 @@ def test_ffn_reads_rows_through_src(dtype, k):
         outs.append(bits_of(yp))
         del keep
     assert np.array_equal(outs[0], outs[1])
-    ref = oracle.expert_ffn(oracle.widen(xp, dtype), offsets, oracle.widen(w13[1], dtype),
-                            oracle.widen(w2[1], dtype))
+    x64, w13l, w2l = (oracle.widen(a, dtype) for a in (xp, w13[1], w2[1]))
+    ref = oracle.expert_ffn(x64, offsets, w13l, w2l)
     got = oracle.widen(outs[1].view(np.uint16) if dtype == "bf16" else outs[1].view(np.float32),
                        dtype)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            check_bound(got[a:b], ref[a:b], swiglu_bound(x64[a:b], w13l[e], w2l[e], dtype),
+                        what=f"fused {dtype} k={k} e={e}")
     tol = (BF16_MAX_ABS, BF16_REL) if dtype == "bf16" else (F32_TOL, F32_TOL)
     check_close(got, ref, *tol, what=f"fused {dtype} k={k}")

@@ -123,3 +123,34 @@ def test_full_stack_stays_finite_with_prenorm(gated):
     print(f"[prenorm] rms of h after {cfg.L} layers: {rms:.3f}; 1-u {1 - eng.stats()[1]:.4f}",
           flush=True)
     assert 0.5 < rms < 50
+
+
+@pytest.mark.parametrize("policy", ["cumutil", "maxutil"])
+def test_prenorm_whole_run_vs_oracle(policy):
+    """The block bench.py times (pre-norm, packed weights, device-driven loop)
+    over a whole Algorithm 1 run against the oracle's run_engine with the
+    pre-norm block, on a reduced stack of the Qwen3 structure: the schedule
+    and the Eq. (3) accumulators exactly, the final hidden states within the
+    tolerance chained over the layers (the GPU rounds h to bf16 after every
+    layer)."""
+    dev = device()
+    cfg = synth.small(synth.CONFIGS["qwen3"], L=6, T=128, n=4, H=512, I=256, E=32, k=4, m=3)
+    W = synth.weights_torch(cfg, 3, dev)
+    logits = np.stack([np.stack([synth.logits(cfg, 3, j, l) for l in range(cfg.L)])
+                       for j in range(cfg.n)])
+    h0 = np.stack([synth.hidden(cfg, 3, j) for j in range(cfg.n)])
+    Wk = tuple(None if w is None else cle.pack_weights(w) for w in W)
+    print(f"[prenorm run] {policy}", flush=True)
+    eng = Engine(Wk, torch.from_numpy(logits).to(dev), to_dev(h0, "bf16", dev), cfg.D, cfg.k,
+                 cle.POLICIES[policy], cfg.m, packed=True, prenorm=True, device_loop=True).run()
+    torch.cuda.synchronize()
+    w13, w2 = oracle.widen(to_host(W[0]), "bf16"), oracle.widen(to_host(W[1]), "bf16")
+    h_ref, trace, acc, u = oracle.run_engine(
+        [oracle.widen(h, "bf16") for h in h0], lambda j, l: logits[j, l], cfg.k, cfg.D, w13, w2,
+        cfg.m, oracle.POLICIES[policy], prenorm=True, eps=cle.NORM_EPS)
+    assert eng.trace == trace, "schedule differs from the oracle's Algorithm 1"
+    a, ug = eng.stats()
+    assert a[:3] == list(acc) and a[3] == len(trace)
+    for j in range(cfg.n):
+        check_close(oracle.widen(to_host(eng.h[j]), "bf16"), h_ref[j], 2e-2 * cfg.L ** 0.5, 1e-2,
+                    what=f"h[{j}] after {cfg.L} layers ({policy})")
