@@ -100,6 +100,9 @@ _sig = {
                                       ctypes.POINTER(_vp), _vp]),
     "cle_pack_weights": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "cle_set_expert_tile": (_i32, [_i32]),
+    "cle_grouped_expert_ffn_noalloc": (_i32, [ctypes.POINTER(FfnDesc), _i32, _vp, _vp, _vp, _vp,
+                                              _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              ctypes.POINTER(_vp), _vp]),
     "cle_combine": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32, _vp]),
     "cle_workload_stats": (_i32, [_vp, _i32, _i32, _i32, _u64, _vp, _vp, _vp]),
     "cle_schedule_step": (_i32, [ctypes.POINTER(_i32), _i32, _i32, _u64, _i32, _i32,
@@ -254,6 +257,26 @@ def grouped_expert_ffn(descs, w13, w2, ws, w13_shared=None, w2_shared=None, even
         arr, len(descs), _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared), L, E, ns, H,
         I2 // 2, _dt(w13), W_PACKED if packed else W_ROWMAJOR, _ptr(ws),
         ws.numel() * ws.element_size(), ev, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def grouped_expert_ffn_noalloc(descs, w13, w2, w13_shared=None, w2_shared=None, events=None,
+                               stream=None, packed=False):
+    """grouped_expert_ffn without a workspace: the library's own fixed scratch
+    (one per GPU) is used; concurrent calls on one GPU race."""
+    L, E, I2, H = w13.shape
+    ns = 0 if w13_shared is None else w13_shared.shape[1]
+    arr = (FfnDesc * len(descs))(*descs)
+    ev = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events: 4 hipEvent_t handles")
+        ev = (_vp * 4)(*events)
+    _check("cle_grouped_expert_ffn_noalloc", _lib.cle_grouped_expert_ffn_noalloc(
+        arr, len(descs), _ptr(w13), _ptr(w2), _ptr(w13_shared), _ptr(w2_shared), L, E, ns, H,
+        I2 // 2, _dt(w13), W_PACKED if packed else W_ROWMAJOR, ev, _stream(stream)))
 
 
 TILE_DEFAULT, TILE_128X256, TILE_256X256, TILE_128X512 = 0, 1, 2, 3

@@ -27,6 +27,7 @@
 #include <hip/hip_ext.h>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "cle_internal.h"
@@ -1375,6 +1376,53 @@ int persistent_grid(int64_t upper_bound_tiles, int resident) {
 
 }  // namespace
 }  // namespace cle
+
+// ---------------------------------------------------------------- no-allocation variant
+// cle_grouped_expert_ffn_noalloc keeps its workspace (tile totals, per-XCD
+// claims, segment table, row-tile prefix) in this file-scope array: one copy
+// per GPU, held until the process ends.  Host code never takes the array's
+// name as an address: the device address is looked up once per device with
+// hipGetSymbolAddress and used from then on.
+namespace cle {
+namespace {
+constexpr size_t kNoAllocScratchBytes = CLE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device, set on the first call there
+
+cle_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return CLE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CLE_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CLE_OK;
+}
+}  // namespace
+}  // namespace cle
+
+extern "C" cle_status cle_grouped_expert_ffn_noalloc(
+    const cle_ffn_desc* d, int32_t n_desc, const void* w13, const void* w2,
+    const void* w13_shared, const void* w2_shared, int32_t L, int32_t E, int32_t n_shared,
+    int32_t H, int32_t I, cle_dtype dt, int32_t w_layout, void* const* phase_events,
+    void* stream) {
+  // the sizes are checked before the scratch is touched; grouped_ffn checks
+  // every other argument
+  if (!d || n_desc < 1 || n_desc > CLE_MAX_DESC || E < 1 || E > CLE_MAX_E || n_shared < 0)
+    return CLE_EINVAL;
+  if (cle_workspace_bytes(CLE_OP_FFN, 0, E, 1, n_shared, n_desc) > cle::kNoAllocScratchBytes)
+    return CLE_EUNSUPPORTED;
+  void* ws = nullptr;
+  const cle_status st = cle::noalloc_scratch(&ws);
+  if (st != CLE_OK) return st;
+  return cle::grouped_ffn(d, n_desc, w13, w2, w13_shared, w2_shared, L, E, n_shared, H, I, dt,
+                          w_layout, ws, cle::kNoAllocScratchBytes, phase_events, nullptr, true,
+                          stream);
+}
 
 extern "C" cle_status cle_set_expert_tile(int32_t tile) {
   if (tile < CLE_TILE_DEFAULT || tile > CLE_TILE_128X512) return CLE_EINVAL;

@@ -13,7 +13,9 @@
  * Conventions shared by every entry point:
  *  - Ownership: the caller allocates and frees every buffer.  The library
  *    never allocates device memory; scratch comes from a caller workspace
- *    sized by cle_workspace_bytes().
+ *    sized by cle_workspace_bytes(), except in
+ *    cle_grouped_expert_ffn_noalloc, whose scratch is a fixed array in the
+ *    library's device code (one per GPU, for the life of the process).
  *  - Pointers are device pointers unless marked HOST.
  *  - Tensors are dense row-major.  bf16 tensors hold IEEE bfloat16 bit
  *    patterns; gates are float32; indices are int32.
@@ -199,6 +201,30 @@ cle_status cle_grouped_expert_ffn(const cle_ffn_desc* d, int32_t n_desc,
                                   int32_t L, int32_t E, int32_t n_shared, int32_t H, int32_t I,
                                   cle_dtype dt, int32_t w_layout, void* ws, size_t ws_bytes,
                                   void* const* phase_events, void* stream);
+
+/*
+ * cle_grouped_expert_ffn_noalloc -- cle_grouped_expert_ffn without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The same kernels and the same results, bit for bit.
+ * Its scratch is a file-scope device array of CLE_NOALLOC_SCRATCH_BYTES
+ * (1 MiB) in the library, one per GPU, held until the process ends; the
+ * call allocates and frees nothing, and the kernels set every byte of scratch
+ * they read on the same call (no clearing between calls).  Calls that overlap
+ * on one GPU (on different streams, or from different host threads) share
+ * that array and race: serialise them.  Arguments as cle_grouped_expert_ffn.
+ * Returns CLE_EUNSUPPORTED when cle_workspace_bytes(CLE_OP_FFN, 0, E, 1,
+ * n_shared, n_desc) exceeds CLE_NOALLOC_SCRATCH_BYTES (e.g. 64 descriptors x
+ * 128 experts fit; 64 x 1024 do not), CLE_EHIP if the array's device address
+ * cannot be found.
+ */
+#define CLE_NOALLOC_SCRATCH_BYTES (1u << 20)
+cle_status cle_grouped_expert_ffn_noalloc(const cle_ffn_desc* d, int32_t n_desc,
+                                          const void* w13, const void* w2,
+                                          const void* w13_shared, const void* w2_shared,
+                                          int32_t L, int32_t E, int32_t n_shared, int32_t H,
+                                          int32_t I, cle_dtype dt, int32_t w_layout,
+                                          void* const* phase_events, void* stream);
 
 /*
  * cle_set_expert_tile -- the output tile of the bf16 expert launches
