@@ -1,19 +1,21 @@
 """Throughput of the cross-layer MoE step on one MI355X.
 
-A timed step is one iteration of Algorithm 1 of EasyBalance over the
-Qwen3-30B-A3B-shaped synthetic stack (48 layers, hidden 2048, 128 experts
-top-8, SwiGLU intermediate 768, D = 8 groups, 4 micro-batches of 2048
-tokens): route + dispatch of the previous RunSet, the workload statistics
-and Schedule(S, m) (CumUtil, m = 3), one grouped expert launch per GEMM phase
-for every RunSet member at its own layer, and the gate-weighted combine.  By
-default the step is one cle_loop_step (the schedule runs on the device and the
-host never waits); --host-loop times the host-driven step instead (workloads
-copied to the host, the host scheduler, then the launches).  When all
-micro-batches have passed layer 48 the loop restarts at layer 0 from the
-initial hidden states.
+A timed step is one whole run of Algorithm 1 of EasyBalance -- every
+micro-batch through every layer -- over the Qwen3-30B-A3B-shaped synthetic
+stack (48 layers, hidden 2048, 128 experts top-8, SwiGLU intermediate 768,
+D = 8 groups, 4 micro-batches of 2048 tokens).  Each of its iterations
+routes and dispatches the previous RunSet, takes the workload statistics and
+Schedule(S, m) (CumUtil, m = 3), runs one grouped expert launch per GEMM
+phase for every RunSet member at its own layer, and the gate-weighted
+combine.  By default an iteration is one cle_loop_step (the schedule runs on
+the device and the host never waits); --host-loop times host-driven
+iterations instead (workloads copied to the host, the host scheduler, then
+the launches).  When all micro-batches have passed layer 48 the loop
+restarts at layer 0 from the initial hidden states, inside the iteration
+that finishes the run, so the timed steps are back-to-back whole runs.
 
 Prints one JSON line (rank 0):
-  value      expert tokens/s over the timed steps (inputs resident in HBM);
+  value      expert tokens/s over the timed whole runs (inputs resident in HBM);
   roofline   the dominant kernel (grouped gate/up GEMM): algorithmic bytes or
              FLOPs per launch / its mean launch time, from start/end HIP
              events that the launch itself records on the library's stream
@@ -455,18 +457,113 @@ def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None, gate=None, prenorm=
                        f"SwiGLU experts, combine); {spent:.1f} s")
 
 
+def run_length(Wk, lt, ht, cfg, policy, m, stream, packed, gate_k, prenorm):
+    """Iterations of Algorithm 1 in one whole run (every micro-batch through
+    every layer), from one device-driven run on the same inputs."""
+    from cross_layer_expert_amd.engine import Engine
+    e = Engine(Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
+               stream=stream, packed=packed, device_loop=True, gate=gate_k, prenorm=prenorm)
+    e.run(chunk=max(1, cfg.L // 2))
+    n = len(e.trace)
+    del e
+    return n
+
+
+def launch_stats(name, g1, g2, W):
+    """Mean time, TFLOP/s, GB/s and binding-roofline fractions of the two GEMM
+    phases over launches with algorithmic work W = (bytes1, bytes2, flops1,
+    flops2), summed over the same launches."""
+    B1, B2, F1, F2 = W
+    t1, t2 = sum(g1) / 1e3, sum(g2) / 1e3
+    K = len(g1)
+
+    def binding(F, B, t):
+        return max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / t
+
+    out = {}
+    for ph, g, t, B, F in (("gate_up", g1, t1, B1, F1), ("down", g2, t2, B2, F2)):
+        out[ph] = dict(mean_us=round(t / K * 1e6, 2), median_us=round(float(np.median(g)) * 1e3, 2),
+                       tflops=round(F / t / 1e12, 1), mfma_peak_frac=round(F / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                       gbs=round(B / t / 1e9, 1), hbm_frac=round(B / t / 1e9 / HBM_PEAK_GBS, 4),
+                       binding_roofline_frac=round(binding(F, B, t), 4),
+                       bound="mfma" if F / B > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+                       else "hbm")
+    return out
+
+
+def prefill_leg(Wk, seed, dev, stream, policy_name, prenorm):
+    """The long-prefill shape (2 micro-batches x 16384 tokens) on the same
+    48 x 128-expert weight stack: one whole device-driven run after a warm-up
+    run, with the expert launches' own events; per-phase MFMA fractions."""
+    import torch
+    import cross_layer_expert_amd as cle
+    import synth
+    from cross_layer_expert_amd.engine import Engine
+    pcfg = synth.CONFIGS["prefill"]
+    t0 = time.time()
+    lg = np.stack([np.stack([synth.logits(pcfg, seed, j, l) for l in range(pcfg.L)])
+                   for j in range(pcfg.n)])
+    lt = torch.from_numpy(lg).to(dev)
+    del lg
+    h0 = np.stack([synth.hidden(pcfg, seed, j) for j in range(pcfg.n)])
+    ht = torch.from_numpy(h0.view(np.int16)).to(dev).view(torch.bfloat16)
+    policy = cle.POLICIES[policy_name]
+    eng = Engine(Wk, lt, ht, pcfg.D, pcfg.k, policy, pcfg.m, stream=stream, packed=True,
+                 device_loop=True, prenorm=prenorm)
+    eng.run(chunk=pcfg.L // 2)                       # warm-up run
+    n_iter = len(eng.trace)
+    eng.reset()
+    hip = HipEvents()
+    evs = [hip.create(4) for _ in range(n_iter)]
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    s0 = time.perf_counter()
+    for i in range(n_iter):
+        eng.step(events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - s0
+    gc.enable()
+    eng.sync_trace()
+    steps = [list(zip(R, layers)) for R, layers in eng.trace]
+    assert eng.sync_trace().ready == 0 and len(steps) == n_iter
+    counts_host = {}
+    for (j, l) in sorted({jl for R in steps for jl in R}):
+        counts_host[(j, l)] = counts_of(eng, j, l).cpu().numpy()
+    W = [0.0, 0.0, 0.0, 0.0]
+    for R in steps:
+        W = [a + b for a, b in zip(W, ffn_work(pcfg, R, counts_host))]
+    g1 = [hip.ms(e[0], e[1]) for e in evs]
+    g2 = [hip.ms(e[2], e[3]) for e in evs]
+    tok = sum(len(R) * pcfg.T * pcfg.k for R in steps)
+    out = dict(workload=workload_name(pcfg), policy=policy_name, m=pcfg.m,
+               iterations=n_iter, run_ms=round(elapsed * 1e3, 2),
+               expert_tokens_per_s=round(tok / elapsed, 1),
+               gemm_mfma_peak_frac=round((W[2] + W[3]) / (sum(g1) + sum(g2)) / 1e9
+                                         / BF16_PEAK_TFLOPS, 4))
+    out.update(launch_stats("prefill", g1, g2, W))
+    out["setup_s"] = round(time.time() - t0 - elapsed, 1)
+    del eng, lt, ht
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps; a step is one whole Algorithm 1 run (every micro-batch "
+                         "through every layer)")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed whole runs before timing")
     ap.add_argument("--config", default="qwen3")
     ap.add_argument("--policy", default="cumutil")
     ap.add_argument("--m", type=int, default=None)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip whole-run and 1-u passes")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the whole-run comparison, 1-u and long-prefill passes")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the long-prefill leg")
     ap.add_argument("--host-loop", action="store_true",
                     help="time the host-driven step (schedule on the host after a wait for the "
                          "workloads) instead of the device-driven one")
@@ -537,14 +634,16 @@ def main():
         gate_k = (cle.pack_weights(gate[0]) if packed else gate[0], gate[1])
     torch.cuda.synchronize()
     K, Wm = args.steps, args.warmup
-    C = min(K, 40)
     device_loop = not args.host_loop
-    # device loop: every step is one cle_loop_step (schedule on the device, no
-    # host wait); when all micro-batches finish, the loop restarts from h0
-    # inside that step
+    # a timed step is one whole run of Algorithm 1; every run of the same
+    # inputs takes the same iterations
+    n_iter = run_length(Wk, lt, ht, cfg, policy, m, stream, packed, gate_k, prenorm)
+    # device loop: every iteration is one cle_loop_step (schedule on the
+    # device, no host wait); when all micro-batches finish, the loop restarts
+    # from h0 inside that iteration
     eng = Engine(Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
                  stream=stream, packed=packed, device_loop=device_loop, restart=device_loop,
-                 log_cap=max(4096, Wm + K + 64), gate=gate_k, prenorm=prenorm)
+                 log_cap=max(4096, (Wm + K) * n_iter + 64), gate=gate_k, prenorm=prenorm)
     hip = HipEvents()
 
     def one_step(e, events=None):
@@ -552,19 +651,20 @@ def main():
             e.reset()
         return e.step(events=events)
 
-    for _ in range(Wm):
+    for _ in range(Wm * n_iter):
         one_step(eng)
     torch.cuda.synchronize()
 
     # the expert launches take their own start/end events (no marker between
     # kernels); Python's cyclic collector stays off while the steps run
-    evs = [hip.create(4) for _ in range(K)]
+    NI = K * n_iter
+    evs = [hip.create(4) for _ in range(NI)]
     steps = []
     gc.collect()
     gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
+    for i in range(NI):
         one_step(eng, events=evs[i])
         if not device_loop:
             R, layers = eng.trace[-1]
@@ -574,32 +674,36 @@ def main():
     gc.enable()
     if device_loop:
         eng.sync_trace()
-        steps = [list(zip(R, layers)) for R, layers in eng.trace[-K:]]
-        assert len(eng.trace) == Wm + K
+        steps = [list(zip(R, layers)) for R, layers in eng.trace[-NI:]]
+        assert len(eng.trace) == (Wm + K) * n_iter
+    # every timed run takes each micro-batch through its remaining layers once
+    units_per_run = sum(cfg.L - s for s in (cfg.start_layers or [0] * cfg.n))
+    assert sum(len(R) for R in steps) == K * units_per_run
 
-    # host-driven steps (host schedule after a wait for the workloads) on the
-    # same buffers: a timed pass for comparison, then a pass with markers
-    # around route + dispatch and after the combine (markers cost a few us of
-    # stream time each, so they stay out of the timed steps above)
+    # host-driven iterations (host schedule after a wait for the workloads) on
+    # the same buffers: one timed whole run for comparison, then a pass with
+    # markers around route + dispatch and after the combine (markers cost a
+    # few us of stream time each, so they stay out of the timed steps above)
     hst = eng if not device_loop else Engine(
         Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers, stream=stream,
         packed=packed, gate=gate_k, prenorm=prenorm)
-    for _ in range(5):
-        one_step(hst)
+    hst.reset()
+    hst.run()
+    hst.reset()
     torch.cuda.synchronize()
-    HK = min(K, 100)
     gc.collect()
     gc.disable()
     h0t = time.perf_counter()
-    for _ in range(HK):
-        one_step(hst)
+    hst.run()
     torch.cuda.synchronize()
-    host_ms = (time.perf_counter() - h0t) / HK * 1e3
+    host_ms = (time.perf_counter() - h0t) * 1e3
     gc.enable()
+    C = min(NI, 40)
     cev = [hip.create(4) for _ in range(C)]
     marks = [hip.create(3) for _ in range(C)]
     sh = stream.cuda_stream
     routed, csteps = [], []
+    hst.reset()
     for i in range(C):
         if hst.done:
             hst.reset()
@@ -620,46 +724,44 @@ def main():
         for (j, l) in need:
             counts_host[(j, l)] = counts_of(eng, j, l).cpu().numpy()
     else:
-        # routing depends on the hidden state: replay the same steps host-driven
-        # from the start (bitwise the same run) and read each member's counts
+        # routing depends on the hidden state: replay one whole run host-driven
+        # (bitwise the same run) and read each member's counts
         rep = Engine(Wk, lt, ht, cfg.D, cfg.k, policy, m, start_layers=cfg.start_layers,
                      stream=stream, packed=packed, gate=gate_k, prenorm=prenorm)
         replayed = []
-        while len(replayed) < Wm + K:
-            if rep.done:
-                rep.reset()
+        while not rep.done:
             R = rep.step()
             replayed.append(list(zip(R, [rep.l[j] - 1 for j in R])))
             for j in R:
                 counts_host.setdefault((j, rep.l[j] - 1), rep.counts[j].cpu().numpy())
-        assert replayed[Wm:] == steps, "replay differs from the timed run"
+        assert replayed * K == steps, "replay differs from the timed run"
         del rep
-    B1 = B2 = F1 = F2 = 0.0
+    Wk_ = [0.0, 0.0, 0.0, 0.0]
     for R in steps:
-        b1, b2, f1, f2 = ffn_work(cfg, R, counts_host)
-        B1, B2, F1, F2 = B1 + b1, B2 + b2, F1 + f1, F2 + f2
+        Wk_ = [a + b for a, b in zip(Wk_, ffn_work(cfg, R, counts_host))]
+    B1, B2, F1, F2 = Wk_
     t1, t2 = sum(g1) / 1e3, sum(g2) / 1e3
     ai1 = F1 / B1
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai1 < ridge:
-        ach = B1 / K / (t1 / K) / 1e9
+        ach = B1 / NI / (t1 / NI) / 1e9
         roof = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4))
     else:
-        ach = F1 / K / (t1 / K) / 1e12
+        ach = F1 / NI / (t1 / NI) / 1e12
         roof = dict(bound="mfma", achieved=round(ach, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(ach / BF16_PEAK_TFLOPS, 4))
-    default_run = args.policy == "cumutil" and args.m is None and args.seed == 0
-    roof["traffic"] = measured_traffic(cfg.name) if default_run else None
+    default_run = args.policy == "cumutil" and args.m is None and args.seed == 0 and \
+        not args.gate and prenorm and device_loop
+    trf = measured_traffic(cfg.name) if default_run else None
+    roof["traffic"] = trf
     roof.update(kernel="ffn_gemm_bf16<1> (grouped gate/up + SwiGLU)",
-                mean_launch_us=round(t1 / K * 1e6, 2),
-                algorithmic_bytes_per_launch=int(B1 / K), flops_per_launch=int(F1 / K))
+                mean_launch_us=round(t1 / NI * 1e6, 2),
+                algorithmic_bytes_per_launch=int(B1 / NI), flops_per_launch=int(F1 / NI))
+    if trf:
+        roof["traffic_over_algorithmic"] = round(trf / (B1 / NI), 4)
 
     gemm_tflops = (F1 + F2) / (t1 + t2) / 1e12
-
-    def binding(F, B, t):
-        """Fraction of the binding roofline: max(FLOP / peak, bytes / HBM) / t."""
-        return max(F / (BF16_PEAK_TFLOPS * 1e12), B / (HBM_PEAK_GBS * 1e9)) / t
 
     # route + dispatch of the previous RunSet, and the combine, from events on
     # the same stream (stream time between the events)
@@ -677,16 +779,17 @@ def main():
     cb_bytes = sum(len(R) for R in csteps) * cb_unit
     t_rd, t_cb = sum(rd_ms) / 1e3, sum(cb_ms) / 1e3
     extras = dict(
+        iterations_per_step=n_iter,
+        ms_per_iteration=round(elapsed / NI * 1e3, 4),
         gemm_tflops=round(gemm_tflops, 1),
         mfma_peak_frac=round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
         gemm_hbm_gbs=round((B1 + B2) / (t1 + t2) / 1e9, 1),
-        gemm_binding_roofline_frac=round(binding(F1 + F2, B1 + B2, t1 + t2), 4),
-        gate_up=dict(mean_us=round(t1 / K * 1e6, 2), median_us=round(float(np.median(g1)) * 1e3, 2),
-                     tflops=round(F1 / t1 / 1e12, 1), gbs=round(B1 / t1 / 1e9, 1),
-                     binding_roofline_frac=round(binding(F1, B1, t1), 4)),
-        down=dict(mean_us=round(t2 / K * 1e6, 2), median_us=round(float(np.median(g2)) * 1e3, 2),
-                  tflops=round(F2 / t2 / 1e12, 1), gbs=round(B2 / t2 / 1e9, 1),
-                  binding_roofline_frac=round(binding(F2, B2, t2), 4)),
+        gemm_binding_roofline_frac=round(
+            max((F1 + F2) / (BF16_PEAK_TFLOPS * 1e12), (B1 + B2) / (HBM_PEAK_GBS * 1e9))
+            / (t1 + t2), 4),
+    )
+    extras.update(launch_stats(cfg.name, g1, g2, Wk_))
+    extras.update(
         route_dispatch=dict(mean_us=round(t_rd / max(len(rd_ms), 1) * 1e6, 2),
                             gbs=round(rd_bytes / t_rd / 1e9, 1) if t_rd else None,
                             bytes_per_microbatch=rd_unit),
@@ -694,7 +797,7 @@ def main():
                      bytes_per_microbatch=cb_unit),
         ffn_share_of_step=round((t1 + t2) / elapsed, 3),
         loop="device" if device_loop else "host",
-        host_loop_ms_per_step=round(host_ms, 4),
+        host_loop_ms_per_step=round(host_ms, 3),
     )
 
     if not args.no_extras and gate is None:
@@ -731,6 +834,12 @@ def main():
                     one_minus_u=round(1 - e2.stats()[1], 4))
                 del e2
         extras["whole_run"] = runs
+    pre = synth.CONFIGS["prefill"]
+    same_stack = (cfg.L, cfg.E, cfg.H, cfg.I, cfg.n_shared, cfg.dtype) == (
+        pre.L, pre.E, pre.H, pre.I, pre.n_shared, pre.dtype)
+    if not args.no_extras and not args.no_prefill and same_stack and cfg.name != "prefill" \
+            and gate is None:
+        extras["prefill"] = prefill_leg(Wk, args.seed, dev, stream, "cumutil", prenorm)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -738,11 +847,17 @@ def main():
         cpu["one_core"] = cpu_baseline(cfg, W, logits, h0, args.cpu_budget / 2, threads=1,
                                        gate=gate, prenorm=prenorm)
 
+    routing = ("hidden state routed through seeded per-layer linear routers plus a Zipf "
+               "expert bias" if gate is not None else
+               f"seeded router logits N(0,1) + {'Zipf' if cfg.bias == 'zipf' else 'normal'} "
+               f"per-layer expert bias")
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "expert tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(elapsed / K * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded router logits with Zipf skew, N(0,1) hidden, N(0,0.02) weights)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": f"synthetic ({routing}, N(0,1) hidden, N(0,0.02) weights); a step is one "
+                f"whole Algorithm 1 run of {n_iter} iterations",
         "config": {"workload": workload_name(cfg), "policy": args.policy if policy != 1 else "b1",
                    "schedule": "device" if device_loop else "host",
                    "routing": "hidden state through the router" if gate is not None
