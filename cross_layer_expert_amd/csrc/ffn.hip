@@ -861,23 +861,30 @@ __device__ __forceinline__ void tile256_nmb(const TileArgs& t, int wave, int lan
 
 // ---------------------------------------------------------------- 512-wide tiles
 // 128 rows x 512 weight rows (phase 1: 256 act columns, phase 2: 512 output
-// columns): each wavefront loads four weight blocks per stage.  What bounds
-// the expert launches on large segments is the traffic that misses L2 (the
-// MALL and HBM side sustains about 6.5 TB/s for the whole chip, L2 hits about
-// five times that): a segment's A rows are read once per column tile, and
-// concurrent tiles of one row tile start too far apart in time to share them
-// in L2, so A comes from HBM once per column tile.  Twice the columns per
-// tile halve those reads (3 instead of 6 column tiles at I = 768, 4 instead of
-// 8 at H = 2048).  A stage (K = 64) is 80 KiB, so the two stages fill the
-// LDS; the loop is the 256-row tile's (two stages, K / 64 even).  Compute
-// layout 1 x 8: each wavefront computes all 128 rows of the four weight
-// blocks it loaded itself.
+// columns): each wavefront loads four weight blocks per stage.  On large
+// segments what bounds the expert launches is operand traffic, and most of
+// what misses L2 is the A rows, which are read once per column tile (the
+// concurrent tiles of one row tile start too far apart in time to share
+// them in L2): twice the columns per tile halve those reads (3 instead of 6
+// column tiles at I = 768, 4 instead of 8 at H = 2048; a third less fetched
+// from HBM on the long-prefill launches).  What a CU can keep in flight is
+// limited, so the ring stays deep: stages of K = 32 (40 KiB), four of them
+// (the whole LDS), three in flight while one is computed.
+// A stage slot is 16 rows x 64 bytes (1 KiB); 16-byte chunk i of row r sits
+// at position r * 4 + (i ^ ((r >> 2) & 3)), so the MFMA operand reads (16
+// rows x one chunk per quarter-wavefront) hit distinct banks; lane p of a
+// load instruction fetches the chunk that belongs at its position p.
+// Compute layout 1 x 8: each wavefront computes all 128 rows of the four
+// weight blocks it loaded itself.
+constexpr int kKS2 = 32;  // K per stage of the 512-wide tile
 struct StageLDS4 {
-  uint4 w[32][2][64];   // [wave * 4 + block][row group][position]
-  uint4 x[kMB][2][64];  // [row block][row group][position]
+  uint4 w[32][64];   // [wave * 4 + block][position]
+  uint4 x[kMB][64];  // [row block][position]
 };
 template <int PHASE, bool PACKED> __shared__ StageLDS4 g_sw0;
 template <int PHASE, bool PACKED> __shared__ StageLDS4 g_sw1;
+template <int PHASE, bool PACKED> __shared__ StageLDS4 g_sw2;
+template <int PHASE, bool PACKED> __shared__ StageLDS4 g_sw3;
 
 template <int PHASE, bool PACKED, int NMB, typename Hook = NoHook>
 __device__ __forceinline__ void tile512_nmb(const TileArgs& t, int wave, int lane,
@@ -889,28 +896,28 @@ __device__ __forceinline__ void tile512_nmb(const TileArgs& t, int wave, int lan
   constexpr int RB = NB;        // weight blocks each wavefront computes (its own)
   constexpr int AM = NMB > 0 ? NMB : 1;
   static_assert(NMB >= 1 && NMB <= kMB, "row blocks per wavefront");
-  const int KT = t.K / kKS;
-  const int lr = lane / 8, lc = (lane % 8) ^ (lane / 8);
-  const uint16_t* wp[NB][2];
+  const int KT = t.K / kKS2;
+  // load side: lane p fetches row lr, chunk lc of a 16-row block (lc is the
+  // chunk whose swizzled position is p)
+  const int lr = lane >> 2, lc = (lane & 3) ^ ((lr >> 2) & 3);
+  // the 64-K packed block holds K stage s in its half s & 1; chunk c of row
+  // rr (of an 8-row group) at rr * 8 + (c ^ rr)
+  const int pk = (lr >> 3) * 512 + (lr & 7) * 64;  // row lr's 128-byte run (elements)
+  const uint16_t* wp[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
+    wp[b] = (b < HB ? t.wlo : t.whi) + (b % HB) * 16 * t.K +
+            (PACKED ? pk : lr * t.K + lc * 8);
+  const uint16_t* xp[XB];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-      wp[b][g] = (b < HB ? t.wlo : t.whi) + (b % HB) * 16 * t.K +
-                 (PACKED ? g * 512 + lane * 8 : (g * 8 + lr) * t.K + lc * 8);
-  const uint16_t* xp[XB][2];
-#pragma unroll
-  for (int b = 0; b < XB; ++b)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int row = min((wave * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
-      const int64_t arow =
-          t.rmap ? static_cast<int64_t>(*(gcint*)(t.rmap + row) / t.kdiv) : row;
-      xp[b][g] = t.A + arow * t.K + lc * 8;
-    }
-  const int rg = (lane % 16) / 8, r8 = lane % 8;
-  const int pos0 = r8 * 8 + ((0 + lane / 16) ^ r8);
-  const int pos1 = r8 * 8 + ((4 + lane / 16) ^ r8);
+  for (int b = 0; b < XB; ++b) {
+    const int row = min((wave * XB + b) * 16 + lr, t.nrows - 1);
+    const int64_t arow = t.rmap ? static_cast<int64_t>(*(gcint*)(t.rmap + row) / t.kdiv) : row;
+    xp[b] = t.A + arow * t.K + lc * 8;
+  }
+  // read side: MFMA operand of lane l is row l % 16, chunk l / 16
+  const int rr = lane & 15;
+  const int pos = rr * 4 + ((lane >> 4) ^ ((rr >> 2) & 3));
 
   f32x4 acc[RB][AM];
 #pragma unroll
@@ -918,65 +925,73 @@ __device__ __forceinline__ void tile512_nmb(const TileArgs& t, int wave, int lan
 #pragma unroll
     for (int mb = 0; mb < AM; ++mb) acc[b][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // request K stage KT_ (of the rotated order) into ST
 #define CLE_ISSUE(ST, KT_)                                                          \
   {                                                                                 \
     int kr = (KT_) + t.rot;                                                         \
     kr -= kr >= KT ? KT : 0;                                                        \
-    const int ko = kr * kKS;                                                        \
+    const int ko = kr * kKS2;                                                       \
+    const int pkc = (kr >> 1) * 1024 + (((kr & 1) * 4 + lc) ^ (lr & 7)) * 8;         \
     _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
-      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
-        dma16(wp[b][g] + (PACKED ? kr * 1024 : ko), &ST.w[wave * NB + b][g][0]);     \
+      dma16(wp[b] + (PACKED ? pkc : ko), &ST.w[wave * NB + b][0]);                  \
     _Pragma("unroll") for (int b = 0; b < XB; ++b)                                  \
-      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
-        dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
+      dma16(xp[b] + ko, &ST.x[wave * XB + b][0]);                                   \
   }
   bf16x8 fb[2][RB], fa[2][AM];
 #define CLE_READ(ST, H)                                                             \
   {                                                                                 \
-    const int pos = (H) == 0 ? pos0 : pos1;                                         \
     _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
-      fb[H][b] = __builtin_bit_cast(bf16x8, ST.w[wave * NB + b][rg][pos]);          \
+      fb[H][b] = __builtin_bit_cast(bf16x8, ST.w[wave * NB + b][pos]);              \
     _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                              \
-      fa[H][mb] = __builtin_bit_cast(bf16x8, ST.x[mb][rg][pos]);                    \
+      fa[H][mb] = __builtin_bit_cast(bf16x8, ST.x[mb][pos]);                        \
   }
 #define CLE_MFMA(H)                                                                 \
   _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                                \
     _Pragma("unroll") for (int b = 0; b < RB; ++b)                                  \
       acc[b][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[H][mb], fb[H][b], acc[b][mb], 0, 0, 0);
-#define CLE_STEP4(CUR, NXT, KT_, ISS)                                               \
+  // Step KT_: stage KT_'s operands are in registers (set KT_ & 1), stages
+  // KT_+1 .. KT_+3 are in the other buffers.  Wait for this wavefront's loads
+  // of stage KT_+1 (W: the loads it may leave in flight), barrier (everyone's
+  // loads of KT_+1 have landed, everyone has read CUR), request stage KT_+4
+  // into CUR, then the MFMAs of stage KT_ while reading stage KT_+1.
+  constexpr int kPerStep = NB + XB;
+#define CLE_STEP(CUR, NXT, KT_, W, ISS)                                             \
   {                                                                                 \
-    wait_vmcnt<0>();                                                                \
+    wait_vmcnt<W>();                                                                \
     stage_barrier();                                                                \
-    if constexpr (ISS) CLE_ISSUE(CUR, (KT_) + 2);                                   \
-    CLE_MFMA(1);                                                                    \
-    CLE_READ(NXT, 0);                                                               \
-    half_step_order<NMB, RB>();                                                     \
-    CLE_MFMA(0);                                                                    \
-    CLE_READ(NXT, 1);                                                               \
+    if constexpr (ISS) CLE_ISSUE(CUR, (KT_) + 4);                                   \
+    CLE_MFMA((KT_) & 1);                                                            \
+    CLE_READ(NXT, ((KT_) + 1) & 1);                                                 \
     half_step_order<NMB, RB>();                                                     \
   }
-  constexpr int kPerStep = 2 * NB + 2 * XB;
-  auto& sa = g_sw0<PHASE, PACKED>;
-  auto& sb = g_sw1<PHASE, PACKED>;
-  CLE_ISSUE(sa, 0);
-  CLE_ISSUE(sb, 1);
+  auto& s0 = g_sw0<PHASE, PACKED>;
+  auto& s1 = g_sw1<PHASE, PACKED>;
+  auto& s2 = g_sw2<PHASE, PACKED>;
+  auto& s3 = g_sw3<PHASE, PACKED>;
+  CLE_ISSUE(s0, 0);
+  CLE_ISSUE(s1, 1);
+  CLE_ISSUE(s2, 2);
+  CLE_ISSUE(s3, 3);
   hook();
-  wait_vmcnt<kPerStep>();
+  wait_vmcnt<3 * kPerStep>();
   stage_barrier();
-  CLE_READ(sa, 0);
-  CLE_MFMA(0);
-  CLE_READ(sa, 1);
+  CLE_READ(s0, 0);
   int kt = 0;
-  for (; kt + 2 < KT; kt += 2) {
-    CLE_STEP4(sa, sb, kt, true);
-    CLE_STEP4(sb, sa, kt + 1, true);
+  for (; kt + 4 < KT; kt += 4) {
+    CLE_STEP(s0, s1, kt, 2 * kPerStep, true);
+    CLE_STEP(s1, s2, kt + 1, 2 * kPerStep, true);
+    CLE_STEP(s2, s3, kt + 2, 2 * kPerStep, true);
+    CLE_STEP(s3, s0, kt + 3, 2 * kPerStep, true);
   }
-  CLE_STEP4(sa, sb, kt, false);  // stage KT-2 in sa, KT-1 in sb
-  CLE_MFMA(1);
+  // stages KT-4 .. KT-1 sit in s0 .. s3 (KT % 4 == 0), all requested
+  CLE_STEP(s0, s1, kt, 2 * kPerStep, false);
+  CLE_STEP(s1, s2, kt + 1, kPerStep, false);
+  CLE_STEP(s2, s3, kt + 2, 0, false);
+  CLE_MFMA(1);  // stage KT-1 (odd)
 #undef CLE_ISSUE
 #undef CLE_READ
 #undef CLE_MFMA
-#undef CLE_STEP4
+#undef CLE_STEP
   wait_vmcnt<0>();
 
   // lane holds rows mb*16 + (lane/16)*4 + i, column lane%16 of each of its
@@ -1082,6 +1097,7 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     __builtin_memcpy(&kw, &segs[tp.si].kdiv, sizeof(kw));
     const int kdiv = static_cast<int16_t>(kw & 0xffff), kkey = (kw >> 16) & 0xffff;
     t.rot = kkey % (K / kKS);
+    if constexpr (kWide4) t.rot *= 2;  // the same K order counted in 32-K stages
     t.nrows = min(TM, sg.rows - row0);
     // The output row stride is laundered per tile: otherwise the compiler
     // hoists every per-row output offset (row * stride, one register per
@@ -1190,9 +1206,9 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
     // first requests overwrite them
     stage_barrier();
     if constexpr (kWide4) {
-      // wavefront 0 leaves the next tile in stage 1's buffer; every wavefront
-      // has read it before the next tile requests stage 1 there
-      uint4* hand = &g_sw1<PHASE, PACKED>.x[0][0][0];
+      // wavefront 0 leaves the next tile in the last stage buffer; every
+      // wavefront has read it before the next tile requests a stage there
+      uint4* hand = &g_sw3<PHASE, PACKED>.x[0][0];
       if (wave == 0 && lane == 0)
         *hand = make_uint4(static_cast<unsigned>(tnext), static_cast<unsigned>(next.si),
                            static_cast<unsigned>(next.nt), static_cast<unsigned>(next.mi));
