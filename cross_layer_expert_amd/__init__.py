@@ -100,6 +100,7 @@ _sig = {
                                       ctypes.POINTER(_vp), _vp]),
     "cle_pack_weights": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _vp]),
     "cle_set_expert_tile": (_i32, [_i32]),
+    "cle_set_fused_thin_rows": (_i32, [_i32]),
     "cle_grouped_expert_ffn_noalloc": (_i32, [ctypes.POINTER(FfnDesc), _i32, _vp, _vp, _vp, _vp,
                                               _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                               ctypes.POINTER(_vp), _vp]),
@@ -288,6 +289,12 @@ def set_expert_tile(tile):
     bitwise the same for every tile): an int or a name of TILES."""
     _check("cle_set_expert_tile", _lib.cle_set_expert_tile(TILES.get(tile, tile)
                                                            if isinstance(tile, str) else tile))
+
+
+def set_fused_thin_rows(rows):
+    """Fused gate/up -> down launch for routed segments of 1 .. rows rows
+    (process-wide; 0 off, -1 the environment decides; results bitwise the same)."""
+    _check("cle_set_fused_thin_rows", _lib.cle_set_fused_thin_rows(int(rows)))
 
 
 def pack_weights(src, dst=None, stream=None):

@@ -103,7 +103,7 @@ struct Seg {
                         // layer and expert only)
   int16_t grank;        // position of the segment in its group
   int16_t gsize;        // segments in the group
-  int32_t pad;
+  int32_t fused;        // 1: run by the fused thin-segment launch, no tiles in the two phases
 };
 // (kdiv/kkey and grank/gsize are read in pairs as 32-bit words, low half first)
 static_assert(sizeof(Seg) == 64 && offsetof(Seg, kdiv) % 4 == 0 &&

@@ -45,7 +45,9 @@ constexpr int kXcds = 8;
 // the per-XCD tile claim counters of the two phases sit in the workspace
 // header after the tile totals: ints [kClaimsOffset, kClaimsOffset + 16)
 constexpr int kClaimsOffset = 16;
-static_assert((kClaimsOffset + 2 * kXcds) * sizeof(int) <= kFfnHeader, "workspace header");
+// then the segment counter of the fused thin-segment launch: int [kClaimsOffset + 16]
+constexpr int kFusedCounter = kClaimsOffset + 2 * kXcds;
+static_assert((kFusedCounter + 1) * sizeof(int) <= kFfnHeader, "workspace header");
 
 struct DescDev {
   int layer, rows;
@@ -73,6 +75,7 @@ struct PlanArgs {
   // the launch that plans the last descriptors also orders the whole table
   // (see order_segments); earlier launches leave these unused
   int order, nseg, tm, n1, n2;
+  int thin;  // > 0: routed segments of 1 .. thin rows go to the fused thin-segment launch
   int* totals;
   int* mscan;
 };
@@ -94,6 +97,12 @@ __device__ __forceinline__ void seg_range(const DescDev& d, int e, int& lo, int&
   hi = min(max(d.offsets[e + 1], lo), d.rows);
 }
 
+// Row tiles of a segment in the two GEMM phases (none for a segment the fused
+// thin-segment launch runs).
+__device__ __forceinline__ int seg_tiles(int rows, int fused, int tm) {
+  return fused ? 0 : (rows + tm - 1) / tm;
+}
+
 // One block over the grouped segment table: the row-tile prefix M over the
 // segments (mscan[s] = row tiles of segments before s), then per segment its
 // group's start m0 = M at the group's first segment, the group's row tiles
@@ -108,7 +117,7 @@ __device__ __forceinline__ void order_segments(Seg* __restrict__ segs, int nseg,
   const int per = (nseg + 1023) / 1024;
   const int lo = min(nseg, tid * per), hi = min(nseg, lo + per);
   int c = 0;
-  for (int s = lo; s < hi; ++s) c += (segs[s].rows + tm - 1) / tm;
+  for (int s = lo; s < hi; ++s) c += seg_tiles(segs[s].rows, segs[s].fused, tm);
   part[tid] = c;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -120,7 +129,7 @@ __device__ __forceinline__ void order_segments(Seg* __restrict__ segs, int nseg,
   int m = part[tid] - c;
   for (int s = lo; s < hi; ++s) {
     mscan[s] = m;
-    m += (segs[s].rows + tm - 1) / tm;
+    m += seg_tiles(segs[s].rows, segs[s].fused, tm);
   }
   if (tid == 1023) {
     mscan[nseg] = m;
@@ -265,17 +274,17 @@ __global__ __launch_bounds__(1024) void ffn_plan(PlanArgs p, Seg* __restrict__ s
     g.m0 = g.gmt = g.moff = 0;
     g.grank = static_cast<int16_t>(prank[jl]);
     g.gsize = static_cast<int16_t>(pcnt[jl]);
-    g.pad = 0;
+    g.fused = p.thin > 0 && g.rows >= 1 && g.rows <= p.thin && g.widx >= 0;
     const int pos = pbase[jl] + e * pcnt[jl] + prank[jl];
     segs[pos] = g;
     if (in_lds) {
-      rows_l[pos] = g.rows;
+      rows_l[pos] = g.fused ? 0 : g.rows;  // tiles of the two phases
       grp_l[pos] = (static_cast<int>(g.gsize) << 16) | static_cast<uint16_t>(g.grank);
     }
   }
   if (p.order) {
     __shared__ int part[1024];
-    if (tid < 2 * kXcds) p.totals[kClaimsOffset + tid] = 0;  // the GEMMs' tile claims
+    if (tid < 2 * kXcds + 1) p.totals[kClaimsOffset + tid] = 0;  // tile claims, fused counter
     __syncthreads();
     if (in_lds)
       order_segments_lds(segs, p.nseg, p.tm, p.n1, p.n2, p.totals, rows_l, grp_l, mscan_l, part);
@@ -309,7 +318,7 @@ __device__ __forceinline__ TilePos locate_tile(const Seg* segs, int nseg, int ti
   int32_t gw;
   __builtin_memcpy(&gw, &segs[lo].grank, sizeof(gw));
   int s = lo - static_cast<int16_t>(gw & 0xffff);
-  while (q >= segs[s].moff + (segs[s].rows + tm - 1) / tm) ++s;
+  while (q >= segs[s].moff + seg_tiles(segs[s].rows, segs[s].fused, tm)) ++s;
   return TilePos{s, nt, q - segs[s].moff};
 }
 
@@ -500,7 +509,7 @@ struct NoHook {
 };
 
 template <int PHASE, int WN, int NB, bool PACKED, int RH, int RG, int NMB, int TR,
-          typename Hook = NoHook>
+          int BUF = PHASE, typename Hook = NoHook>
 __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane,
                                          const Hook& hook = Hook()) {
   // lane-derived offsets (operand positions, epilogue rows) are recomputed per
@@ -613,9 +622,10 @@ __device__ __forceinline__ void tile_nmb(const TileArgs& t, int wave, int lane,
   }
 
   static_assert(kStages == 3, "the pipeline below is written for 3 buffers");
-  auto& st0 = g_st0<PHASE, WN, NB, PACKED>;
-  auto& st1 = g_st1<PHASE, WN, NB, PACKED>;
-  auto& st2 = g_st2<PHASE, WN, NB, PACKED>;
+  // BUF names the stage buffers (a kernel that runs both phases shares one set)
+  auto& st0 = g_st0<BUF, WN, NB, PACKED>;
+  auto& st1 = g_st1<BUF, WN, NB, PACKED>;
+  auto& st2 = g_st2<BUF, WN, NB, PACKED>;
   // (K / 64 < 3 only on small shapes: the prologue then re-requests the last
   // stage into a buffer no step reads; the final wait covers it.)
   CLE_ISSUE(st0, 0);
@@ -1229,6 +1239,97 @@ __global__ __launch_bounds__(64 * WN, 1) void ffn_gemm_bf16(const Seg* __restric
   }
 }
 
+// ---------------------------------------------------------------- fused thin segments
+// Gate/up and down of one thin segment (1 .. 16 rows) in one workgroup, in
+// one launch: the six gate/up column tiles, then the eight down column tiles
+// read the segment's Act rows this workgroup has just written (still in its
+// L2), with no launch boundary between the phases.  Segments are taken from
+// the table through a counter; the segment's tiles and K order are those of
+// the two-phase kernels, so its outputs are bitwise the same.  Built for the
+// K-loop tails of H = 2048 and I = 768 (4 and 2 steps).
+template <bool PACKED, int TR1, int TR2>
+__global__ __launch_bounds__(512, 1) void ffn_fused_thin(const Seg* __restrict__ segs, int nseg,
+                                                        int* __restrict__ counter, Weights wts,
+                                                        int H, int I) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int l16 = lane % 16;
+  const int rg = wave / 4;  // row group of the 2 x 4 compute layout
+  __shared__ int s_pick;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      gint* cp = (gint*)counter;
+      asm volatile("" : "+v"(cp));
+      s_pick = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const int si = __builtin_amdgcn_readfirstlane(s_pick);
+    __syncthreads();
+    if (si >= nseg) break;
+    if (!segs[si].fused) continue;
+    const Seg sg = segs[si];
+    int32_t kw;
+    __builtin_memcpy(&kw, &segs[si].kdiv, sizeof(kw));
+    const int kdiv = static_cast<int16_t>(kw & 0xffff), kkey = (kw >> 16) & 0xffff;
+    TileArgs t;
+    t.nrows = sg.rows;
+    t.bias = nullptr;
+    // gate/up: 128 act columns per column tile
+    {
+      const uint16_t* W = static_cast<const uint16_t*>(seg_weights(wts, sg, 1, H, I, 2));
+      t.K = H;
+      t.rot = kkey % (H / kKS);
+      t.A = sg.a;
+      t.rmap = sg.rmap;
+      t.kdiv = sg.rmap ? kdiv : 1;
+      t.out = static_cast<uint16_t*>(sg.act);
+      int ldo = I;
+      asm volatile("" : "+s"(ldo));
+      t.ldo = ldo;
+      for (int nt = 0; nt < I / 128; ++nt) {
+        const int wlo = (nt * 8 + wave) * 16;
+        t.wlo = W + static_cast<int64_t>(wlo) * H;
+        t.whi = W + static_cast<int64_t>(I + wlo) * H;
+        t.col = nt * 128 + l16;
+        if (rg == 0)
+          tile_nmb<1, 8, 2, PACKED, 2, 0, 1, TR1>(t, wave, lane);
+        else
+          tile_nmb<1, 8, 2, PACKED, 2, 1, 0, TR1>(t, wave, lane);
+        stage_barrier();
+      }
+    }
+    // every wavefront's Act stores have completed before any wavefront's
+    // down loads read them, and the CU's L1 holds no older copy of those rows
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // down: 256 output columns per column tile
+    {
+      const uint16_t* W = static_cast<const uint16_t*>(seg_weights(wts, sg, 2, H, I, 2));
+      t.K = I;
+      t.rot = kkey % (I / kKS);
+      t.A = static_cast<const uint16_t*>(sg.act);
+      t.rmap = nullptr;
+      t.kdiv = 1;
+      t.out = static_cast<uint16_t*>(sg.y);
+      int ldo = H;
+      asm volatile("" : "+s"(ldo));
+      t.ldo = ldo;
+      for (int nt = 0; nt < H / 256; ++nt) {
+        const int wlo = (nt * 8 + wave) * 32;
+        t.wlo = W + static_cast<int64_t>(wlo) * I;
+        t.whi = W + static_cast<int64_t>(wlo + 16) * I;
+        t.col = nt * 256 + l16;
+        if (rg == 0)
+          tile_nmb<2, 8, 2, PACKED, 2, 0, 1, TR2, 1>(t, wave, lane);
+        else
+          tile_nmb<2, 8, 2, PACKED, 2, 1, 0, TR2, 1>(t, wave, lane);
+        stage_barrier();
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- f32 tiles (exact-order reference path)
 template <int PHASE>
 __global__ __launch_bounds__(256) void ffn_gemm_f32(const Seg* __restrict__ segs, int nseg,
@@ -1383,6 +1484,20 @@ WideTile wide_tile_shape() {
   return g_tile_choice == CLE_TILE_DEFAULT ? env : static_cast<WideTile>(g_tile_choice);
 }
 
+// Fused thin-segment launch (cle_set_fused_thin_rows): routed segments of 1
+// .. r rows go to ffn_fused_thin; an explicit choice, else the environment's
+// CLE_FUSE_THIN read once, else off.
+int g_fuse_choice = -1;
+
+int fuse_thin_rows() {
+  static const int env = [] {
+    const char* v = getenv("CLE_FUSE_THIN");
+    const int r = v ? atoi(v) : 0;
+    return r < 0 ? 0 : (r > 16 ? 16 : r);
+  }();
+  return g_fuse_choice >= 0 ? g_fuse_choice : env;
+}
+
 int persistent_grid(int64_t upper_bound_tiles, int resident) {
   int64_t g = resident;
   if (upper_bound_tiles < g) g = upper_bound_tiles;
@@ -1440,6 +1555,12 @@ extern "C" cle_status cle_grouped_expert_ffn_noalloc(
                           stream);
 }
 
+extern "C" cle_status cle_set_fused_thin_rows(int32_t rows) {
+  if (rows < -1 || rows > 16) return CLE_EINVAL;
+  cle::g_fuse_choice = rows;
+  return CLE_OK;
+}
+
 extern "C" cle_status cle_set_expert_tile(int32_t tile) {
   if (tile < CLE_TILE_DEFAULT || tile > CLE_TILE_128X512) return CLE_EINVAL;
   cle::g_tile_choice = tile;
@@ -1477,8 +1598,13 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
   if (dt == CLE_BF16 ? (H < 128 || H % 128) : (H < 64 || H % 64)) return CLE_EINVAL;
   const bool wide = dt == CLE_BF16 && I % 128 == 0 && H % 256 == 0;
   const bool tall = wide && wide_tile_shape() == kTile256x256;
+  // the fused thin-segment launch: 128 x 256 tiles with the K-loop tails of
+  // H = 2048 and I = 768 (K / 64 = 32 and 12)
+  const auto tail_of = [](int K) { return 2 + (K / kKS - 3) % 3; };
   const bool wide4 = wide && wide_tile_shape() == kTile128x512 && I % 256 == 0 && H % 512 == 0;
   const int tm = dt == CLE_BF16 ? (tall ? kTM2 : kTM) : kBM;
+  const int thin = wide && !tall && !wide4 && H / kKS >= 3 && I / kKS >= 3 &&
+                           tail_of(H) == 4 && tail_of(I) == 2 ? fuse_thin_rows() : 0;
   const int tn1 = dt == CLE_BF16 ? (wide4 ? 256 : wide ? 128 : 64) : kBNF;
   const int tn2 = dt == CLE_BF16 ? (wide4 ? 512 : wide ? 256 : 128) : kBNF;
   if (n_shared > 0 && (!w13_shared || !w2_shared)) return CLE_EINVAL;
@@ -1541,6 +1667,7 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
     p.tm = tm;
     p.n1 = I / tn1;
     p.n2 = H / tn2;
+    p.thin = thin;
     p.totals = totals;
     p.mscan = mscan;
     ffn_plan<<<dim3(1), dim3(1024), 0, s>>>(p, segs);
@@ -1561,7 +1688,11 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
                             static_cast<const int*>(totals), claims, wts, H, I);
       return true;
     }
-    return !e0 || (hipEventRecord(e0, s) == hipSuccess && hipEventRecord(e1, s) == hipSuccess);
+    // no tiles: the events this phase was given are recorded back to back
+    bool rec = true;
+    if (e0) rec = rec && hipEventRecord(e0, s) == hipSuccess;
+    if (e1) rec = rec && hipEventRecord(e1, s) == hipSuccess;
+    return rec;
   };
   // The 8-wavefront bf16 kernel of a phase, with the K-loop tail its K needs.
   auto run_wide = [&](auto phase, auto pk, int K, int64_t ub, hipEvent_t e0, hipEvent_t e1,
@@ -1586,6 +1717,22 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
   using PKF = std::false_type;
   static int occ_c1[64], occ_c2[64], occ_f1[64], occ_f2[64], occ_c1p[64], occ_c2p[64];
   bool ok;
+  if (thin > 0) {
+    // the fused thin segments first (the gate/up events bracket both launches)
+    static int occ_ft[64], occ_ff[64];
+    int* counter = totals + kFusedCounter;
+    if (packed)
+      hipExtLaunchKernelGGL(ffn_fused_thin<true, 4, 2>, dim3(resident_blocks(
+                                ffn_fused_thin<true, 4, 2>, occ_ft, 512)),
+                            dim3(512), 0, s, ev[0], nullptr, 0, static_cast<const Seg*>(segs),
+                            nseg, counter, wts, H, I);
+    else
+      hipExtLaunchKernelGGL(ffn_fused_thin<false, 4, 2>, dim3(resident_blocks(
+                                ffn_fused_thin<false, 4, 2>, occ_ff, 512)),
+                            dim3(512), 0, s, ev[0], nullptr, 0, static_cast<const Seg*>(segs),
+                            nseg, counter, wts, H, I);
+    ev[0] = nullptr;
+  }
   if (wide)
     ok = packed ? run_wide(P1(), PKT(), H, ub1, ev[0], ev[1], claims1)
                 : run_wide(P1(), PKF(), H, ub1, ev[0], ev[1], claims1);

@@ -250,6 +250,22 @@ cle_status cle_grouped_expert_ffn_noalloc(const cle_ffn_desc* d, int32_t n_desc,
 cle_status cle_set_expert_tile(int32_t tile);
 
 /*
+ * cle_set_fused_thin_rows -- the fused gate/up -> down launch for thin
+ * segments (process-wide; takes effect at the next expert launch).  With
+ * rows in 1 .. 16, routed segments of 1 .. rows rows run in one extra launch
+ * in which one workgroup computes a segment's gate/up column tiles and then
+ * its down column tiles, reading the Act rows it has just written, instead
+ * of in the two phase launches (the paper's expert FFN per segment, fused
+ * across the phases).  0: off; -1 (the default): the environment variable
+ * CLE_FUSE_THIN decides (off when unset).  Used only with 128 x 256 tiles
+ * where H / 64 and I / 64 leave K-loop tails of 4 and 2 steps (H = 2048,
+ * I = 768 among them); results are bitwise the same either way.  Not
+ * synchronised with launches in flight on other host threads.  Returns
+ * CLE_EINVAL for rows outside -1 .. 16.
+ */
+cle_status cle_set_fused_thin_rows(int32_t rows);
+
+/*
  * cle_pack_weights -- re-lays out n_mat row-major bf16 matrices [R, K] (src)
  * into the CLE_W_PACKED layout (dst, same size, must not overlap src), for
  * cle_grouped_expert_ffn with w_layout = CLE_W_PACKED.  Pack each of w13
