@@ -49,10 +49,12 @@ PROFILE = os.path.join(ROOT, "profiles", "ffn_gemm_gate_up_qwen3.md")
 KERNEL_SOURCES = ("cross_layer_expert_amd/csrc/ffn.hip", "cross_layer_expert_amd/csrc/cle_internal.h")
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, algorithmic_per_launch: float):
     """HBM bytes per gate/up launch from the committed rocprofv3 FETCH_SIZE +
-    WRITE_SIZE summary, or None when that summary is for another workload or
-    the kernel sources changed since the counters were taken."""
+    WRITE_SIZE summary, or None when that summary is for another workload,
+    the kernel sources changed since the counters were taken, or its launches
+    carried different work (algorithmic bytes per launch more than 0.5 %
+    apart: another mix of launches than the ones timed here)."""
     try:
         text = open(PROFILE).read()
     except OSError:
@@ -67,6 +69,9 @@ def measured_traffic(workload: str):
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     if fields.get("workload") != workload or fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    alg = float(fields.get("algorithmic_bytes_per_launch", "nan"))
+    if not abs(alg - algorithmic_per_launch) <= 0.005 * algorithmic_per_launch:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -753,7 +758,7 @@ def main():
                     frac=round(ach / BF16_PEAK_TFLOPS, 4))
     default_run = args.policy == "cumutil" and args.m is None and args.seed == 0 and \
         not args.gate and prenorm and device_loop
-    trf = measured_traffic(cfg.name) if default_run else None
+    trf = measured_traffic(cfg.name, B1 / NI) if default_run else None
     roof["traffic"] = trf
     roof.update(kernel="ffn_gemm_bf16<1> (grouped gate/up + SwiGLU)",
                 mean_launch_us=round(t1 / NI * 1e6, 2),
