@@ -20,6 +20,12 @@ struct Vec<uint16_t> {
   // rows in flight take 4 registers each instead of 8
   using Raw = uint4;
   __device__ static Raw load_raw(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  // a row no other wavefront reads: non-temporal (it does not displace reused lines)
+  __device__ static Raw load_once(const uint16_t* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
   __device__ static void unpack(const Raw& v, float* f) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -43,6 +49,7 @@ struct Vec<float> {
   static constexpr int N = 4;
   using Raw = float4;
   __device__ static Raw load_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static Raw load_once(const float* p) { return load_raw(p); }
   __device__ static void unpack(const Raw& v, float* f) {
     f[0] = v.x;
     f[1] = v.y;
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs args, int T_, 
       typename Vec<T>::Raw raw[KMAX > 0 ? KMAX : 1];
 #pragma unroll
       for (int s = 0; s < KMAX; ++s)
-        if (d[s] >= 0) raw[s] = Vec<T>::load_raw(yp + static_cast<int64_t>(d[s]) * H + c);
+        if (d[s] >= 0) raw[s] = Vec<T>::load_once(yp + static_cast<int64_t>(d[s]) * H + c);
 #pragma unroll
       for (int s = 0; s < KMAX; ++s)
         if (d[s] >= 0) {
