@@ -79,7 +79,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 // NT: element type of the rows to normalise in the same launch, or void.
-template <int VPL, typename NT>
+// KSEL: slots the selected scores are kept for (k <= KSEL); the LDS a block
+// holds, and so the blocks a CU runs at once, scale with it.
+template <int VPL, typename NT, int KSEL = CLE_MAX_E>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E, int k) {
   const int j = blockIdx.y;
   if constexpr (!std::is_void<NT>::value) {
@@ -101,8 +103,8 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs args, int T, int E
   }
   int* __restrict__ idx = args.idx[j];
   float* __restrict__ gate = args.gate[j];
-  __shared__ float zsel[kRouteWaves][CLE_MAX_E];
-  __shared__ int esel[kRouteWaves][CLE_MAX_E];
+  __shared__ float zsel[kRouteWaves][KSEL];
+  __shared__ int esel[kRouteWaves][KSEL];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * kRouteWaves + wave;
@@ -168,7 +170,12 @@ void launch_route_kernel(const RouteArgs& a, int n, int T, int E, int k, hipStre
   const int rb = (T + kRouteWaves - 1) / kRouteWaves;
   const dim3 grid(std::is_void<NT>::value ? rb : 2 * rb, n), block(256);
   const int vpl = (E + kWave - 1) / kWave;
-  if (vpl <= 1)
+  if (k <= kWave && vpl <= 2) {  // the common shapes: 2 KiB of LDS per block
+    if (vpl <= 1)
+      route_kernel<1, NT, kWave><<<grid, block, 0, s>>>(a, T, E, k);
+    else
+      route_kernel<2, NT, kWave><<<grid, block, 0, s>>>(a, T, E, k);
+  } else if (vpl <= 1)
     route_kernel<1, NT><<<grid, block, 0, s>>>(a, T, E, k);
   else if (vpl <= 2)
     route_kernel<2, NT><<<grid, block, 0, s>>>(a, T, E, k);
