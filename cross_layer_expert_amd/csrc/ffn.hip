@@ -1496,14 +1496,23 @@ enum WideTile { kTile128x256 = CLE_TILE_128X256, kTile256x256 = CLE_TILE_256X256
                 kTile128x512 = CLE_TILE_128X512 };
 int g_tile_choice = CLE_TILE_DEFAULT;
 
-WideTile wide_tile_shape() {
-  static const WideTile env = [] {
+// The tile of a launch whose descriptors hold `rows` rows in all over
+// n_desc x E experts: an explicit choice, else the environment's CLE_TILE
+// read once, else 256 x 256 when the segments average at least 512 rows (the
+// long-prefill shapes: each weight block is read by half as many tiles; 2-3 %
+// faster there, measured) and 128 x 256 otherwise (thin segments would leave
+// most of a 256-row tile empty).
+WideTile wide_tile_shape(int64_t rows, int n_desc, int E) {
+  static const int env = [] {
     const char* v = getenv("CLE_TILE");
-    if (v && !strcmp(v, "256x256")) return kTile256x256;
-    if (v && !strcmp(v, "128x512")) return kTile128x512;
-    return kTile128x256;
+    if (v && !strcmp(v, "128x256")) return static_cast<int>(kTile128x256);
+    if (v && !strcmp(v, "256x256")) return static_cast<int>(kTile256x256);
+    if (v && !strcmp(v, "128x512")) return static_cast<int>(kTile128x512);
+    return 0;
   }();
-  return g_tile_choice == CLE_TILE_DEFAULT ? env : static_cast<WideTile>(g_tile_choice);
+  const int c = g_tile_choice != CLE_TILE_DEFAULT ? g_tile_choice : env;
+  if (c != 0) return static_cast<WideTile>(c);
+  return rows >= static_cast<int64_t>(512) * n_desc * E ? kTile256x256 : kTile128x256;
 }
 
 // Fused thin-segment launch (cle_set_fused_thin_rows): routed segments of 1
@@ -1619,11 +1628,14 @@ cle_status grouped_ffn(const cle_ffn_desc* d, int32_t n_desc, const void* w13, c
   if (I < 64 || I % 64) return CLE_EINVAL;
   if (dt == CLE_BF16 ? (H < 128 || H % 128) : (H < 64 || H % 64)) return CLE_EINVAL;
   const bool wide = dt == CLE_BF16 && I % 128 == 0 && H % 256 == 0;
-  const bool tall = wide && wide_tile_shape() == kTile256x256;
+  int64_t all_rows = 0;
+  for (int j = 0; j < n_desc; ++j) all_rows += d[j].rows > 0 ? d[j].rows : 0;
+  const WideTile shape = wide_tile_shape(all_rows, n_desc, E);
+  const bool tall = wide && shape == kTile256x256;
   // the fused thin-segment launch: 128 x 256 tiles with the K-loop tails of
   // H = 2048 and I = 768 (K / 64 = 32 and 12)
   const auto tail_of = [](int K) { return 2 + (K / kKS - 3) % 3; };
-  const bool wide4 = wide && wide_tile_shape() == kTile128x512 && I % 256 == 0 && H % 512 == 0;
+  const bool wide4 = wide && shape == kTile128x512 && I % 256 == 0 && H % 512 == 0;
   const int tm = dt == CLE_BF16 ? (tall ? kTM2 : kTM) : kBM;
   const int thin = wide && !tall && !wide4 && H / kKS >= 3 && I / kKS >= 3 &&
                            tail_of(H) == 4 && tail_of(I) == 2 ? fuse_thin_rows() : 0;

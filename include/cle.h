@@ -232,9 +232,12 @@ cle_status cle_grouped_expert_ffn_noalloc(const cle_ffn_desc* d, int32_t n_desc,
  * cle_loop_step call).  A tuning choice only: the results are bitwise the
  * same for every tile, since each output element is the same sequence of
  * MFMAs over the same K order.
- *   CLE_TILE_DEFAULT  (0) the library's default (CLE_TILE_128X256, or the
- *                     shape named by the environment variable CLE_TILE,
- *                     "128x256" / "256x256" / "128x512", when it is set);
+ *   CLE_TILE_DEFAULT  (0) the library's choice per launch: CLE_TILE_256X256
+ *                     when the descriptors' rows average at least 512 per
+ *                     expert (rows summed over the descriptors, divided by
+ *                     n_desc * E), else CLE_TILE_128X256; or the shape named
+ *                     by the environment variable CLE_TILE, "128x256" /
+ *                     "256x256" / "128x512", when it is set;
  *   CLE_TILE_128X256  (1) 128 rows x 256 weight rows;
  *   CLE_TILE_256X256  (2) 256 rows x 256 weight rows;
  *   CLE_TILE_128X512  (3) 128 rows x 512 weight rows, used where I % 256 == 0
