@@ -415,6 +415,119 @@ def group_fit(cfg, seed, dev, reps=3, n_sets=96):
                       **results}), flush=True)
 
 
+def ep_projection(cfg, seed, dev, reps=2):
+    """The expert time of whole runs under expert parallelism, projected from
+    launches measured on this GPU: D GPUs, GPU d holding group d's experts of
+    every layer (E/D per layer), each step waiting for its slowest group
+    (EasyBalance's Eq. (2): the step's expert time is set by the peak group).
+
+    For each policy the library's host scheduler plans a whole run from the
+    per-(micro-batch, layer) workloads; every step is then launched once per
+    group over exactly that group's segments of the step's members (the
+    segments GPU d would receive; other experts empty), timed by the launch's
+    own events (start of gate/up to end of down), median of `reps` passes in
+    a seeded random order.  Reported per policy: steps, 1-u, the projected
+    expert time (sum over steps of the slowest group), and the sum over steps
+    and groups (the same work done by this one GPU group by group).  Expert
+    compute only: no all-to-all, no attention."""
+    import torch
+    import cross_layer_expert_amd as cle
+    from cross_layer_expert_amd.engine import Engine
+    W, lt, ht, _, _ = setup(cfg, seed, dev)
+    packed = cfg.dtype == "bf16"
+    Wk = tuple(None if w is None else cle.pack_weights(w) for w in W) if packed else W
+    stream = torch.cuda.current_stream()
+    eng = Engine(Wk, lt, ht, cfg.D, cfg.k, cle.POLICY_B0_ALONE, 1, stream=stream,
+                 packed=packed)
+    hip = HipEvents()
+    G = cfg.E // cfg.D
+    n, L, D = cfg.n, cfg.L, cfg.D
+    off, src = {}, {}
+    for j in range(n):
+        for l in range(L):
+            saved = eng.l[j]
+            eng.l[j] = l
+            eng.route_dispatch(j)
+            eng.l[j] = saved
+            off[(j, l)] = eng.offsets[j].clone()
+            src[(j, l)] = eng.src[j].clone()
+    torch.cuda.synchronize()
+    off_h = {u: o.cpu().numpy().astype(np.int64) for u, o in off.items()}
+    gof, w_table = {}, [[None] * L for _ in range(n)]
+    for u, o in off.items():
+        oh = off_h[u]
+        w_table[u[0]][u[1]] = np.array([oh[(d + 1) * G] - oh[d * G] for d in range(D)], np.int32)
+        for d in range(D):
+            lo, hi = int(oh[d * G]), int(oh[(d + 1) * G])
+            gof[(u, d)] = (torch.clamp(o, lo, hi) - lo, lo, hi - lo)
+    lj0 = list(cfg.start_layers) if cfg.start_layers else [0] * n
+
+    def plan(policy, m):
+        lj, steps = list(lj0), []
+        S = [j for j in range(n) if lj[j] < L]
+        while S:
+            w = np.zeros((n, D), np.int32)
+            for j in S:
+                w[j] = w_table[j][lj[j]]
+            R = cle.ids_of(cle.schedule_step(w, cle.mask_of(S), m, policy))
+            steps.append([(j, lj[j]) for j in R])
+            for j in R:
+                lj[j] += 1
+            S = [j for j in S if lj[j] < L]
+        return steps
+
+    policies = [("b0", cle.POLICY_B0_ALONE, 1), ("b1", cle.POLICY_B1_LOCKSTEP, n),
+                ("cumutil", cle.POLICY_CUMUTIL, min(cfg.m, n)),
+                ("maxutil", cle.POLICY_MAXUTIL, min(cfg.m, n))]
+    plans = {name: plan(pol, m) for name, pol, m in policies}
+    pts = [(name, s_, d) for name, _, _ in policies for s_ in range(len(plans[name]))
+           for d in range(D)]
+    rng = np.random.default_rng(seed + 2000)
+    times = np.zeros((reps, len(pts)))
+    for r in range(reps):
+        evs = [hip.create(4) for _ in pts]
+        for i in rng.permutation(len(pts)):
+            name, s_, d = pts[i]
+            descs = []
+            for u in plans[name][s_]:
+                j, l = u
+                go, lo, rows = gof[(u, d)]
+                dd = cle.FfnDesc.from_buffer_copy(eng.descs[j])
+                dd.layer = l
+                dd.rows = rows
+                dd.offsets = go.data_ptr()
+                dd.src = src[u][lo:].data_ptr()
+                dd.shared_rows = 0
+                dd.x_shared = dd.act_shared = dd.y_shared = None
+                descs.append(dd)
+            cle.grouped_expert_ffn(descs, eng.w13, eng.w2, eng.ws_ffn, events=evs[i],
+                                   stream=stream, packed=packed)
+        torch.cuda.synchronize()
+        times[r] = [hip.ms(e[0], e[3]) * 1e3 for e in evs]
+    t = np.median(times, axis=0)
+    res, idx = {}, 0
+    for name, _, _ in policies:
+        ns = len(plans[name])
+        tt = t[idx:idx + ns * D].reshape(ns, D)
+        idx += ns * D
+        num = den = 0
+        for st in plans[name]:
+            Wd = np.sum([w_table[j][l] for j, l in st], axis=0)
+            num += int(Wd.sum())
+            den += int(Wd.max())
+        res[name] = dict(steps=ns, one_minus_u=round(1.0 - num / (D * den), 4),
+                         projected_ep_expert_ms=round(float(tt.max(axis=1).sum()) / 1e3, 3),
+                         one_gpu_group_by_group_ms=round(float(tt.sum()) / 1e3, 3))
+    b0 = res["b0"]["projected_ep_expert_ms"]
+    for name in res:
+        res[name]["vs_b0"] = round(res[name]["projected_ep_expert_ms"] / b0, 4)
+    print(json.dumps({"metric": "projected expert-parallel expert time per whole run "
+                                "(sum over steps of the slowest group's measured launch)",
+                      "config": {"workload": workload_name(cfg), "D": D, "m": cfg.m,
+                                 "seed": seed, "reps": reps},
+                      "policies": res}), flush=True)
+
+
 def cpu_baseline(cfg, W, logits, h0, budget_s, threads=None, gate=None, prenorm=True):
     """The CPU oracle on (micro-batch, layer) units of the same workload:
     route, dispatch, float64 SwiGLU experts (numpy matmul) and the combine of
@@ -584,6 +697,10 @@ def main():
     ap.add_argument("--group-fit", action="store_true",
                     help="print the per-group expert time against w_d (one group's share of "
                          "each unit, as one GPU of an expert-parallel step) instead of the step")
+    ap.add_argument("--ep-projection", action="store_true",
+                    help="print the projected expert-parallel expert time of whole runs per "
+                         "policy (each step's slowest group, measured per group) instead of "
+                         "the step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -606,6 +723,9 @@ def main():
     cfg = synth.CONFIGS[args.config]
     if args.group_fit:
         group_fit(cfg, args.seed, dev)
+        return
+    if args.ep_projection:
+        ep_projection(cfg, args.seed, dev)
         return
     m = args.m if args.m is not None else cfg.m
     policy = cle.POLICIES[args.policy]
@@ -823,7 +943,16 @@ def main():
     if not args.no_extras:
         # measured whole runs: cross-layer (timed policy) vs one (j, l) per step
         runs = {}
-        for name, pol, mm in (("b0", cle.POLICY_B0_ALONE, 1), (args.policy, policy, m)):
+        # one (j, l) per step; all micro-batches at the same layer (on one GPU
+        # the fastest: a layer's weights are read once for every micro-batch);
+        # the timed policy
+        cands = [("b0", cle.POLICY_B0_ALONE, 1), ("b1", cle.POLICY_B1_LOCKSTEP, cfg.n),
+                 (args.policy, policy, m)]
+        seen = set()
+        for name, pol, mm in cands:
+            if (pol, mm) in seen:
+                continue
+            seen.add((pol, mm))
             for dl in (False, True):
                 e2 = Engine(Wk, lt, ht, cfg.D, cfg.k, pol, mm, start_layers=cfg.start_layers,
                             stream=stream, packed=packed, device_loop=dl, gate=gate_k,
