@@ -168,29 +168,40 @@ def ffn_work(cfg, members, counts_host):
     return b1, b2, f1, f2
 
 
-def schedule_only_u(w_table, D, policy, m, start_layers=None):
-    """1-u of Algorithm 1 over a full run, from the per-(micro-batch, layer)
-    workloads w_table[j][l] (length D), with the library's host scheduler.
-    Returns (1-u, steps, sum of members' own peaks / sum of step peaks)."""
+def plan_run(w_table, D, policy, m, start_layers=None):
+    """The steps of one whole run of Algorithm 1 with the library's host
+    scheduler, from the per-(micro-batch, layer) workloads w_table[j][l]
+    (length D): a list of RunSets, each a list of (micro-batch, layer)."""
     import cross_layer_expert_amd as cle
     n, L = len(w_table), len(w_table[0])
     lj = list(start_layers) if start_layers else [0] * n
     S = [j for j in range(n) if lj[j] < L]
-    num = den = sep = steps = 0
+    steps = []
     while S:
         w = np.zeros((n, D), np.int32)
         for j in S:
             w[j] = w_table[j][lj[j]]
         R = cle.ids_of(cle.schedule_step(w, cle.mask_of(S), m, policy))
-        Wd = w[R].sum(axis=0)
-        num += int(Wd.sum())
-        den += int(Wd.max())
-        sep += int(w[R].max(axis=1).sum())
-        steps += 1
+        steps.append([(j, lj[j]) for j in R])
         for j in R:
             lj[j] += 1
         S = [j for j in S if lj[j] < L]
-    return 1.0 - num / (D * den), steps, sep / den
+    return steps
+
+
+def schedule_only_u(w_table, D, policy, m, start_layers=None):
+    """1-u of Algorithm 1 over a full run, from the per-(micro-batch, layer)
+    workloads w_table[j][l] (length D), with the library's host scheduler.
+    Returns (1-u, steps, sum of members' own peaks / sum of step peaks)."""
+    num = den = sep = 0
+    steps = plan_run(w_table, D, policy, m, start_layers)
+    for st in steps:
+        w = np.array([w_table[j][l] for j, l in st], np.int64)
+        Wd = w.sum(axis=0)
+        num += int(Wd.sum())
+        den += int(Wd.max())
+        sep += int(w.max(axis=1).sum())
+    return 1.0 - num / (D * den), len(steps), sep / den
 
 
 def same_peak(w_table, run):
@@ -460,26 +471,10 @@ def ep_projection(cfg, seed, dev, reps=2):
         for d in range(D):
             lo, hi = int(oh[d * G]), int(oh[(d + 1) * G])
             gof[(u, d)] = (torch.clamp(o, lo, hi) - lo, lo, hi - lo)
-    lj0 = list(cfg.start_layers) if cfg.start_layers else [0] * n
-
-    def plan(policy, m):
-        lj, steps = list(lj0), []
-        S = [j for j in range(n) if lj[j] < L]
-        while S:
-            w = np.zeros((n, D), np.int32)
-            for j in S:
-                w[j] = w_table[j][lj[j]]
-            R = cle.ids_of(cle.schedule_step(w, cle.mask_of(S), m, policy))
-            steps.append([(j, lj[j]) for j in R])
-            for j in R:
-                lj[j] += 1
-            S = [j for j in S if lj[j] < L]
-        return steps
-
     policies = [("b0", cle.POLICY_B0_ALONE, 1), ("b1", cle.POLICY_B1_LOCKSTEP, n),
                 ("cumutil", cle.POLICY_CUMUTIL, min(cfg.m, n)),
                 ("maxutil", cle.POLICY_MAXUTIL, min(cfg.m, n))]
-    plans = {name: plan(pol, m) for name, pol, m in policies}
+    plans = {name: plan_run(w_table, D, pol, m, cfg.start_layers) for name, pol, m in policies}
     pts = [(name, s_, d) for name, _, _ in policies for s_ in range(len(plans[name]))
            for d in range(D)]
     rng = np.random.default_rng(seed + 2000)

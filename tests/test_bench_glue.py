@@ -22,6 +22,20 @@ def test_schedule_only_matches_oracle(policy, m, start):
     assert abs(om - (1 - float(u))) < 1e-12
 
 
+@pytest.mark.parametrize("policy", sorted(oracle.POLICIES))
+@pytest.mark.parametrize("m,start", [(1, None), (3, None), (2, (0, 2, 5, 1, 0))])
+def test_plan_run_is_the_oracle_schedule(policy, m, start):
+    """The whole-run plan the expert-parallel projection launches: every step's
+    members and their layers equal the oracle's Algorithm 1 trace."""
+    rng = np.random.default_rng(len(policy) * 7 + m)
+    n, L, D = 5, 6, 4
+    wt = rng.integers(0, 40, size=(n, L, D))
+    steps = bench.plan_run(wt, D, oracle.POLICIES[policy], m, start)
+    trace, _, _ = oracle.run_schedule_only([[list(r) for r in wj] for wj in wt], n, L, D, m,
+                                           oracle.POLICIES[policy], start_layers=start)
+    assert steps == [list(zip(R, ls)) for R, ls in trace]
+
+
 def test_same_peak_matches_oracle():
     rng = np.random.default_rng(3)
     for D in (2, 4, 8):
