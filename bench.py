@@ -604,6 +604,74 @@ def launch_stats(name, g1, g2, W):
     return out
 
 
+def vendor_gemm(dev, groups, rows, H, I, reps=10):
+    """Same-box context for the MFMA fractions (not part of the path): the
+    vendor libraries' bf16 batched GEMM (torch.bmm through hipBLASLt and
+    through rocBLAS; the faster is reported) on uniform batches of `groups`
+    experts x `rows` rows at the expert shapes, gate/up [rows, H] x [H, 2I]
+    and down [rows, I] x [I, H], timed with events on torch's stream.
+    Operands are contiguous (batched products with a transposed right operand
+    are avoided on this platform)."""
+    import torch
+    libs = (("hipblaslt", "cublaslt"), ("rocblas", "cublas"))
+    before = torch.backends.cuda.preferred_blas_library()
+    out = {}
+    try:
+        for name, K, N in (("gate_up", H, 2 * I), ("down", I, H)):
+            a = torch.randn(groups, rows, K, device=dev).to(torch.bfloat16)
+            b = torch.randn(groups, K, N, device=dev).to(torch.bfloat16).contiguous()
+            c = torch.empty(groups, rows, N, device=dev, dtype=torch.bfloat16)
+            per = {}
+            for lib, key in libs:
+                torch.backends.cuda.preferred_blas_library(key)
+                for _ in range(3):
+                    torch.bmm(a, b, out=c)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    torch.bmm(a, b, out=c)
+                e1.record()
+                torch.cuda.synchronize()
+                per[lib] = e0.elapsed_time(e1) / reps
+            lib = min(per, key=per.get)
+            tf = 2.0 * groups * rows * K * N / (per[lib] * 1e-3) / 1e12
+            out[name] = dict(shape=f"{groups} x ({rows} x {K}) x ({K} x {N})", library=lib,
+                             mean_us=round(per[lib] * 1e3, 1),
+                             us_by_library={k: round(v * 1e3, 1) for k, v in per.items()},
+                             tflops=round(tf, 1), mfma_peak_frac=round(tf / BF16_PEAK_TFLOPS, 4))
+            del a, b, c
+    finally:
+        torch.backends.cuda.preferred_blas_library(before)
+    torch.cuda.empty_cache()
+    return out
+
+
+def hbm_stream(dev, gib=4, reps=5):
+    """Same-box context for the HBM fractions (not part of the path): the rate
+    of torch's device copy over a `gib` GiB bf16 tensor (bytes read +
+    written)."""
+    import torch
+    n = gib << 29
+    a = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_()
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: b.copy_(a), 4 * n),):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = dict(gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         hbm_frac=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    out["bytes"] = 2 * n
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def prefill_leg(Wk, seed, dev, stream, policy_name, prenorm):
     """The long-prefill shape (2 micro-batches x 16384 tokens) on the same
     48 x 128-expert weight stack: one whole device-driven run after a warm-up
@@ -655,9 +723,15 @@ def prefill_leg(Wk, seed, dev, stream, policy_name, prenorm):
                gemm_mfma_peak_frac=round((W[2] + W[3]) / (sum(g1) + sum(g2)) / 1e9
                                          / BF16_PEAK_TFLOPS, 4))
     out.update(launch_stats("prefill", g1, g2, W))
-    out["setup_s"] = round(time.time() - t0 - elapsed, 1)
     del eng, lt, ht
     torch.cuda.empty_cache()
+    # the vendor GEMM at the mean expert shape of one (micro-batch, layer)
+    # unit: every expert of a layer with T * k / E rows
+    ven = vendor_gemm(dev, pcfg.E, pcfg.T * pcfg.k // pcfg.E, pcfg.H, pcfg.I)
+    for ph in ("gate_up", "down"):
+        ven[ph]["ours_over_vendor"] = round(out[ph]["mfma_peak_frac"] / ven[ph]["mfma_peak_frac"], 3)
+    out["vendor_gemm"] = ven
+    out["setup_s"] = round(time.time() - t0 - elapsed, 1)
     return out
 
 
@@ -969,6 +1043,8 @@ def main():
     if not args.no_extras and not args.no_prefill and same_stack and cfg.name != "prefill" \
             and gate is None:
         extras["prefill"] = prefill_leg(Wk, args.seed, dev, stream, "cumutil", prenorm)
+    if not args.no_extras and cfg.dtype == "bf16":
+        extras["hbm_stream"] = hbm_stream(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
