@@ -85,9 +85,10 @@ inline int64_t dispatch_chunks(int64_t A) { return (A + kDispatchChunk - 1) / kD
 // One (micro-batch, expert) segment of a grouped expert launch.  Segments
 // are stored grouped by (layer, expert): the segments of the micro-batches at
 // the same layer using the same expert sit next to each other, ordered by
-// micro-batch, and a group's tiles are ordered by column tile, then by the
-// group's row tiles, so the tiles that read one block of weight rows run
-// back to back (on one XCD) whichever micro-batch their rows come from.
+// micro-batch, and a group's tiles are ordered by column tile (or by blocks
+// of a few column tiles), then by the group's row tiles, so the tiles that
+// read one block of weight rows run close together (on one XCD) whichever
+// micro-batch their rows come from.
 struct Seg {
   const uint16_t* a;    // phase-1 A rows (bf16 or f32 storage; byte pointer semantics by dtype)
   void* act;            // phase-1 output / phase-2 A rows
