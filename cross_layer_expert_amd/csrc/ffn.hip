@@ -862,6 +862,12 @@ __device__ __forceinline__ void tile256_nmb(const TileArgs& t, int wave, int lan
 #undef CLE_STEP2
   wait_vmcnt<0>();
 
+  // The down phase's output rows are stored non-temporally: only the combine
+  // reads them, once, in a later launch, so they need not displace the weight
+  // and A lines the next tiles reuse (long-prefill down 2-3 % faster, its
+  // combine unchanged; on the 128-row tiles of the thinner shapes the same
+  // stores sped the down launch by 2 % but slowed the combine by more, since
+  // its rows were then no longer in the last-level cache).
   const int g4 = lane / 16;
   const int col = t.col + cg * RH * 16 * (PHASE == 1 ? HB : NB);
 #pragma unroll
@@ -880,7 +886,7 @@ __device__ __forceinline__ void tile256_nmb(const TileArgs& t, int wave, int lan
                   bf16_hw(silu_hw(acc[u * NB + b][mb][i]) * acc[u * NB + HB + b][mb][i]);
         } else {
 #pragma unroll
-          for (int b = 0; b < RB; ++b) o[b * 16] = bf16_hw(acc[b][mb][i]);
+          for (int b = 0; b < RB; ++b) __builtin_nontemporal_store(bf16_hw(acc[b][mb][i]), &o[b * 16]);
         }
       }
     }
