@@ -766,23 +766,39 @@ __device__ __forceinline__ void tile256_nmb(const TileArgs& t, int wave, int lan
   const int KT = t.K / kKS;
   // load side: this lane fetches row lr of each 8-row group, chunk lc
   const int lr = lane / 8, lc = (lane % 8) ^ (lane / 8);
-  const uint16_t* wp[NB][2];
+  // Which wavefronts request a stage.  The two wavefronts of a SIMD belong to
+  // different row groups, and the SIMD issues for the first row group's
+  // wavefront first, so the second one finishes every step alone.  In the
+  // gate/up phase (K = H, long K loops) the first row group's wavefronts
+  // request the whole stage, their own blocks and those of the wavefront four
+  // above them, and the second row group's request nothing, which shifts
+  // issue slots towards the wavefronts that finish last (gate/up 1-3 %
+  // faster, measured; in the down phase, with 11-step K loops, it was 4 %
+  // slower, so there every wavefront requests its own blocks).
+  constexpr int LW = PHASE == 1 ? (RG == 0 ? 2 : 0) : 1;
+  constexpr int LWA = LW > 0 ? LW : 1;
+  const int64_t wshift = static_cast<int64_t>(4 * 16 * (PHASE == 1 ? HB : NB)) * t.K;
+  const uint16_t* wp[LWA][NB][2];
+#pragma unroll
+  for (int v = 0; v < LWA; ++v)
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int g = 0; g < 2; ++g)
-      wp[b][g] = (b < HB ? t.wlo : t.whi) + (b % HB) * 16 * t.K +
-                 (PACKED ? g * 512 + lane * 8 : (g * 8 + lr) * t.K + lc * 8);
-  const uint16_t* xp[XB][2];
+      wp[v][b][g] = (b < HB ? t.wlo : t.whi) + v * wshift + (b % HB) * 16 * t.K +
+                    (PACKED ? g * 512 + lane * 8 : (g * 8 + lr) * t.K + lc * 8);
+  const uint16_t* xp[LWA][XB][2];
+#pragma unroll
+  for (int v = 0; v < LWA; ++v)
 #pragma unroll
   for (int b = 0; b < XB; ++b)
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       // rows past the tile repeat its last row (never stored)
-      const int row = min((wave * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
+      const int row = min(((wave + 4 * v) * XB + b) * 16 + g * 8 + lr, t.nrows - 1);
       const int64_t arow =
           t.rmap ? static_cast<int64_t>(*(gcint*)(t.rmap + row) / t.kdiv) : row;
-      xp[b][g] = t.A + arow * t.K + lc * 8;
+      xp[v][b][g] = t.A + arow * t.K + lc * 8;
     }
   const int rg = (lane % 16) / 8, r8 = lane % 8;
   const int pos0 = r8 * 8 + ((0 + lane / 16) ^ r8);
@@ -799,12 +815,14 @@ __device__ __forceinline__ void tile256_nmb(const TileArgs& t, int wave, int lan
     int kr = (KT_) + t.rot;                                                         \
     kr -= kr >= KT ? KT : 0;                                                        \
     const int ko = kr * kKS;                                                        \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                  \
-      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
-        dma16(wp[b][g] + (PACKED ? kr * 1024 : ko), &ST.w[wave * NB + b][g][0]);     \
-    _Pragma("unroll") for (int b = 0; b < XB; ++b)                                  \
-      _Pragma("unroll") for (int g = 0; g < 2; ++g)                                 \
-        dma16(xp[b][g] + ko, &ST.x[wave * XB + b][g][0]);                           \
+    _Pragma("unroll") for (int v = 0; v < LW; ++v) {                                \
+      _Pragma("unroll") for (int b = 0; b < NB; ++b)                                \
+        _Pragma("unroll") for (int g = 0; g < 2; ++g)                               \
+          dma16(wp[v][b][g] + (PACKED ? kr * 1024 : ko), &ST.w[(wave + 4 * v) * NB + b][g][0]); \
+      _Pragma("unroll") for (int b = 0; b < XB; ++b)                                \
+        _Pragma("unroll") for (int g = 0; g < 2; ++g)                               \
+          dma16(xp[v][b][g] + ko, &ST.x[(wave + 4 * v) * XB + b][g][0]);            \
+    }                                                                               \
   }
   bf16x8 fb[2][RB], fa[2][AM];
 #define CLE_READ(ST, H)                                                             \
@@ -838,7 +856,7 @@ __device__ __forceinline__ void tile256_nmb(const TileArgs& t, int wave, int lan
     CLE_READ(NXT, 1);                                                               \
     half_step_order<NMB, RB>();                                                     \
   }
-  constexpr int kPerStep = 2 * NB + 2 * XB;
+  constexpr int kPerStep = LW * (2 * NB + 2 * XB);
   auto& sa = g_sb0<PHASE, PACKED>;
   auto& sb = g_sb1<PHASE, PACKED>;
   CLE_ISSUE(sa, 0);
